@@ -1,0 +1,103 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
+
+This module holds no part of the attention arithmetic: it only draws numbers and
+rounds them to the storage type, so both the HIP path and the oracle can be fed
+the very same values.
+
+Recipe: NumPy PCG64 `default_rng(seed)`; float32 standard normals drawn in the
+order Q, K, V, dO, each over its whole [B, H, T, d] shape; Q and K optionally
+multiplied by a spread (3 for the large-logit cross-attention workload); bf16
+tensors are the float32 draws rounded to nearest-even, and the oracle widens
+exactly those bf16 values to float64.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+BASE_SEED = 20261201
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    out = (rounded >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Tq: int
+    Tk: int
+    d: int
+    dtype: str          # "f32" or "bf16"
+    causal: bool
+    backward: bool      # the workload includes the backward pass
+    qk_spread: float = 1.0
+    seed: int = BASE_SEED
+
+    def flops_fwd(self) -> float:
+        """4 B H Tq Tk d, halved when causal (square causal: visible pairs ~ T^2 / 2)."""
+        f = 4.0 * self.B * self.H * self.Tq * self.Tk * self.d
+        return f / 2 if self.causal else f
+
+    def flops_bwd(self) -> float:
+        """Five tile products against the forward's two: 2.5 x forward."""
+        return 2.5 * self.flops_fwd()
+
+
+WORKLOADS = {
+    "fwd_f32_b1h1_t256_d64": Workload("fwd_f32_b1h1_t256_d64", 1, 1, 256, 256, 64, "f32", False, False,
+                                      seed=BASE_SEED + 1),
+    "causal_bf16_b8h32_t4096_d128": Workload("causal_bf16_b8h32_t4096_d128", 8, 32, 4096, 4096, 128, "bf16",
+                                             True, False, seed=BASE_SEED + 2),
+    "causal_bf16_b4h16_t16384_d64": Workload("causal_bf16_b4h16_t16384_d64", 4, 16, 16384, 16384, 64, "bf16",
+                                             True, True, seed=BASE_SEED + 3),
+    "causal_bf16_b1h24_t65536_d256": Workload("causal_bf16_b1h24_t65536_d256", 1, 24, 65536, 65536, 256, "bf16",
+                                              True, False, seed=BASE_SEED + 4),
+    "cross_bf16_b16h16_tq1024_tk8192_d128": Workload("cross_bf16_b16h16_tq1024_tk8192_d128", 16, 16, 1024, 8192,
+                                                     128, "bf16", False, True, qk_spread=3.0,
+                                                     seed=BASE_SEED + 5),
+}
+
+
+def draw(B, H, Tq, Tk, d, dtype, seed, qk_spread=1.0, with_do=False):
+    """Draw Q, K, V (and dO) as NumPy arrays.
+
+    bf16: uint16 bit patterns; f32: float32.  Returns a dict with keys
+    'q', 'k', 'v' (and 'do').
+    """
+    rng = np.random.default_rng(seed)
+    shapes = [("q", (B, H, Tq, d)), ("k", (B, H, Tk, d)), ("v", (B, H, Tk, d))]
+    if with_do:
+        shapes.append(("do", (B, H, Tq, d)))
+    out = {}
+    for name, shp in shapes:
+        x = rng.standard_normal(shp, dtype=np.float32)
+        if name in ("q", "k") and qk_spread != 1.0:
+            x *= np.float32(qk_spread)
+        out[name] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    return out
+
+
+def draw_workload(w: Workload, with_do=None):
+    return draw(w.B, w.H, w.Tq, w.Tk, w.d, w.dtype, w.seed, w.qk_spread,
+                w.backward if with_do is None else with_do)
+
+
+def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact float64 values of a drawn array (bf16 bits or float32)."""
+    return bf16_bits_to_f32(a).astype(np.float64) if dtype == "bf16" else np.asarray(a, np.float64)

@@ -1,0 +1,190 @@
+"""Exact attention by its definition, in float64 on the CPU (the oracle).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg; never by the HIP library or its binding.
+
+Pages cited (title, then section):
+  [Atlas] "FlashAttention -- IO-Aware Exact Attention" (atlas.blal.pro wiki)
+  [ZtF]   "FlashAttention", zerotofrontier.app efficient-attention, textbook section 12.3
+  [LDD]   "FlashAttention & IO-awareness", llmdeepdive.com lesson 7.7
+  [Blog]  hemanths.vercel.app, "attention_training"
+
+FlashAttention reaches the result of standard attention exactly, only the
+floating-point order differs ([Atlas] "Online softmax: the trick that makes
+tiling exact"; [ZtF] "The forward pass", the paragraph on why the result is
+exactly attention).  So the oracle is the plain definition, not the tiled
+algorithm:
+
+  forward   S = c Q K^T with c the scale (1/sqrt(d) by default)
+            ([ZtF] "The forward pass" step 2.2; [Blog] "Standard Attention:
+            What Actually Happens");
+            causal: query r sees key l iff l <= r, otherwise S = -inf
+            ([ZtF] "The causal mask, and the tiles you never visit"; top-left
+            alignment when Tq != Tk);
+            P = softmax(S) row-wise with the row maximum subtracted,
+            O = P V ([Atlas] "Standard attention, and why it's wasteful");
+            lse_r = m_r + ln sum_l exp(S_rl - m_r), natural log of the scaled
+            and masked scores ([ZtF] "The forward pass" step 3 and "What the
+            forward pass leaves behind"; [Atlas] "Recomputation in the
+            backward pass").
+  backward  for the loss sum(O * dO) ([ZtF] "The backward pass, derived"):
+            dV = P^T dO, dP = dO V^T, D_r = dO_r . O_r (Observation 2),
+            dS = P * (dP - D 1^T) (Observation 3), dQ = c dS K, dK = c dS^T Q
+            (the scale sits in S = c Q K^T, so it multiplies dQ and dK and not
+            dV).  The page's displayed backward equations did not survive
+            extraction; this is the textbook chain rule that its prose states
+            entry by entry, pinned by finite differences in the tests.
+
+Every function works on one (batch, head) slice with NumPy float64 and library
+matmuls; there is no tiling, fusion or reordering beyond the definition.  The
+batched wrappers loop over heads (a thread pool only runs independent heads at
+the same time).  Inputs that were bf16 on the GPU are widened to float64, which
+is exact.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = [
+    "scores_head", "probs_head", "forward_head", "backward_head",
+    "forward", "backward", "default_scale",
+]
+
+
+def default_scale(d: int) -> float:
+    """c = 1/sqrt(d_k) ([ZtF] "The backward pass, derived", definition of c)."""
+    return 1.0 / math.sqrt(d)
+
+
+def _visible(Tk: int, rows: np.ndarray, causal: bool) -> np.ndarray | None:
+    """Boolean [len(rows), Tk]: key l visible to query r.  Causal keeps l <= r
+    ([ZtF] "The causal mask, and the tiles you never visit"); None = all."""
+    if not causal:
+        return None
+    return np.arange(Tk)[None, :] <= rows[:, None]
+
+
+def scores_head(q, k, scale, causal, rows=None):
+    """Scaled, masked scores S[rows, :] = c q k^T with -inf where masked."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    S = scale * (q[rows] @ k.T)
+    vis = _visible(k.shape[0], rows, causal)
+    if vis is not None:
+        S = np.where(vis, S, -np.inf)
+    return S
+
+
+def _softmax_rows(S):
+    """Row softmax with the row maximum subtracted; also returns lse = m + ln l."""
+    m = S.max(axis=1)
+    E = np.exp(S - m[:, None])          # exp(-inf) = 0 for masked entries
+    l = E.sum(axis=1)
+    return E / l[:, None], m + np.log(l)
+
+
+def probs_head(q, k, scale, causal, rows=None):
+    """P[rows, :] = softmax(S) and lse[rows] for one head."""
+    return _softmax_rows(scores_head(q, k, scale, causal, rows))
+
+
+def forward_head(q, k, v, scale, causal, rows=None):
+    """O[rows] = softmax(c q k^T) v and lse[rows] for one head.
+
+    q [Tq, d], k [Tk, d], v [Tk, dv].  Each output row depends only on its own
+    query and all keys, so a subset `rows` is computed exactly by the same
+    definition (used where the full T x T matrix would not fit in memory).
+    """
+    P, lse = probs_head(q, k, scale, causal, rows)
+    return P @ np.asarray(v, dtype=np.float64), lse
+
+
+def backward_head(q, k, v, do, scale, causal):
+    """Gradients of sum(O * dO) for one head: returns dQ, dK, dV, O, lse, D."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    P, lse = probs_head(q, k, scale, causal)
+    O = P @ v
+    dV = P.T @ do
+    dP = do @ v.T
+    D = np.sum(do * O, axis=1)
+    dS = P * (dP - D[:, None])
+    dQ = scale * (dS @ k)
+    dK = scale * (dS.T @ q)
+    return dQ, dK, dV, O, lse, D
+
+
+def _heads(B, H, heads):
+    return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+
+
+def _pool(workers):
+    n = workers or os.cpu_count() or 1
+    return ThreadPoolExecutor(max_workers=max(1, n)), n
+
+
+def _one_blas_thread():
+    """Context limiting BLAS to one thread per worker when threadpoolctl exists."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None):
+    """Batched forward over [B, H, T, d] arrays.
+
+    heads: optional list of (b, h) pairs to compute (others are left NaN);
+    rows: optional query-row subset applied to every selected head.
+    Returns O [B, H, n_rows, d] and lse [B, H, n_rows] in float64.
+    """
+    B, H, Tq, _ = Q.shape
+    n = Tq if rows is None else len(rows)
+    O = np.full((B, H, n, V.shape[3]), np.nan)
+    L = np.full((B, H, n), np.nan)
+    todo = _heads(B, H, heads)
+
+    def run(bh):
+        b, h = bh
+        O[b, h], L[b, h] = forward_head(Q[b, h], K[b, h], V[b, h], scale, causal, rows)
+
+    ex, nw = _pool(workers)
+    with _one_blas_thread() if nw > 1 else _nullctx(), ex:
+        list(ex.map(run, todo))
+    return O, L
+
+
+def backward(Q, K, V, dO, scale, causal, heads=None, workers=None):
+    """Batched backward over [B, H, T, d] arrays; returns dQ, dK, dV, O, lse."""
+    B, H, Tq, d = Q.shape
+    Tk = K.shape[2]
+    dQ = np.full((B, H, Tq, d), np.nan)
+    dK = np.full((B, H, Tk, d), np.nan)
+    dV = np.full((B, H, Tk, V.shape[3]), np.nan)
+    O = np.full((B, H, Tq, V.shape[3]), np.nan)
+    L = np.full((B, H, Tq), np.nan)
+    todo = _heads(B, H, heads)
+
+    def run(bh):
+        b, h = bh
+        dQ[b, h], dK[b, h], dV[b, h], O[b, h], L[b, h], _ = backward_head(
+            Q[b, h], K[b, h], V[b, h], dO[b, h], scale, causal)
+
+    ex, nw = _pool(workers)
+    with _one_blas_thread() if nw > 1 else _nullctx(), ex:
+        list(ex.map(run, todo))
+    return dQ, dK, dV, O, L
+
+
+def _nullctx():
+    import contextlib
+    return contextlib.nullcontext()
