@@ -1,0 +1,107 @@
+/*
+ * fa.h -- exact scaled-dot-product attention, computed tile by tile with the
+ * online-softmax rescale, for AMD Instinct MI355X (gfx950).  C ABI of libfa.so.
+ *
+ * Pages cited (title, then section):
+ *   [Atlas] "FlashAttention -- IO-Aware Exact Attention" (atlas.blal.pro wiki)
+ *   [ZtF]   "FlashAttention", zerotofrontier.app textbook section 12.3
+ *
+ * Operation ([ZtF] "The picture, a grid of tiles" and "The forward pass"):
+ * for every batch b < B and head h < H independently, with S = scale * Q K^T,
+ * P = softmax(S) row-wise and O = P V, plus one log-sum-exp per query row,
+ * lse_r = ln sum_l exp(S_rl) ([ZtF] "What the forward pass leaves behind";
+ * [Atlas] "Recomputation in the backward pass").  With `causal` set, query r
+ * sees key l only when l <= r (top-left alignment, also when Tq != Tk) ([ZtF]
+ * "The causal mask, and the tiles you never visit").  The backward pass returns
+ * the gradients of sum(O * dO) from Q, K, V, O, dO and lse alone, recomputing
+ * the probabilities tile by tile ([ZtF] "The backward pass, derived").
+ *
+ * Layout: every tensor is dense row-major with the head dimension fastest:
+ *   Q, O, dO, dQ   [B][H][Tq][d]      K, V, dK, dV   [B][H][Tk][d]
+ *   lse            [B][H][Tq] float32 (natural log)
+ * Element type: FA_BF16 (bfloat16 storage, float32 accumulation) or FA_F32.
+ * Supported head widths: d in {64, 128, 256}.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; device
+ * buffers must be 16-byte aligned.  The library keeps no state between calls
+ * except the per-device module handles HIP itself keeps.  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL = the null stream): FA_OK means
+ * every launch was accepted, and faults surface at the caller's next
+ * synchronisation.  All argument checks run before any device work; on an
+ * error nothing is launched and no output is touched.  NaN or Inf inputs are
+ * not checked: they propagate to the outputs.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,       /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = -2,      /* B, H, Tq or Tk < 1, or a grid dimension overflows   */
+  FA_ERR_HEADDIM = -3,    /* d not in {64, 128, 256}                             */
+  FA_ERR_DTYPE = -4,      /* unknown dtype, or an unsupported dtype combination  */
+  FA_ERR_SCALE = -5,      /* scale not finite or not > 0                         */
+  FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than fa_bwd_workspace_bytes */
+  FA_ERR_LAUNCH = -7,     /* the HIP runtime rejected a launch                   */
+  FA_ERR_ALIGN = -8       /* a device pointer is not 16-byte aligned             */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * Forward pass ([ZtF] "The forward pass", steps 1-3; FlashAttention-2 order:
+ * one workgroup per query block, one sweep over the key/value blocks, O and
+ * lse written once).
+ *   Q [B][H][Tq][d], K and V [B][H][Tk][d]  (dtype)          in
+ *   O [B][H][Tq][d] (dtype), lse [B][H][Tq] (float32)         out
+ *   scale   the factor on Q K^T; the usual choice is 1/sqrt(d)
+ *   causal  0 = full attention, 1 = query r sees keys l <= r
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
+           int B, int H, int Tq, int Tk, int d, float scale, int causal,
+           int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: the row terms D_r = dO_r . O_r
+ * ([ZtF] "The backward pass, derived", Observation 2; float32 [B][H][Tq]) and,
+ * unless grad_dtype is FA_F32, a float32 dQ accumulator [B][H][Tq][d] that
+ * receives the per-key-block contributions ("Which loop goes outside?").
+ * Returns 0 for invalid arguments.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, int grad_dtype);
+
+/*
+ * Backward pass by recomputation ([ZtF] "The backward pass, derived"):
+ *   Q, K, V, O, dO (dtype), lse (float32, as written by fa_fwd)      in
+ *   dQ [B][H][Tq][d], dK and dV [B][H][Tk][d] (grad_dtype)           out
+ * grad_dtype: FA_BF16 or FA_F32 for bfloat16 inputs; FA_F32 for float32
+ * inputs.  The dQ contributions of different key blocks are summed with
+ * float32 atomic additions, so dQ may differ in its last bits between runs
+ * ([ZtF] "Which loop goes outside?"); dK and dV are deterministic.
+ * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes,
+ * 16-byte aligned, owned by the caller; its contents on entry do not matter.
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* lse, void* dQ, void* dK, void* dV,
+           int B, int H, int Tq, int Tk, int d, float scale, int causal,
+           int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for an fa_status value (never NULL). */
+const char* fa_strerror(int status);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,189 @@
+"""Exact attention for AMD Instinct MI355X (gfx950): Python binding of libfa.so.
+
+The binding only marshals arguments: it checks torch tensors (dtype, shape,
+contiguity, device), passes their device pointers and the current HIP stream to
+the C ABI declared in include/fa.h, and turns error codes into exceptions.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind -- if libfa.so is missing or fails to load, calls raise.
+
+    import torch, io_aware_exact_02_amd as fa
+    O, lse = fa.forward(q, k, v, causal=True)                # q,k,v: [B,H,T,d] bf16/fp32
+    dQ, dK, dV = fa.backward(q, k, v, O, dO, lse, causal=True)
+
+The lower-level names mirror the C entry points one to one (fa_fwd, fa_bwd,
+fa_bwd_workspace_bytes, fa_strerror) and write into caller-provided outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA_F32", "FA_BF16", "FAError", "LIB_PATH", "library", "fa_fwd", "fa_bwd",
+    "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
+    "EXPORTED_SYMBOLS",
+]
+
+FA_F32 = 0
+FA_BF16 = 1
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero fa_status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_strerror(status)} (fa_status {status})")
+
+
+def library() -> ctypes.CDLL:
+    """Load libfa.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m io_aware_exact_02_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def fa_strerror(status: int) -> str:
+    return library().fa_strerror(int(status)).decode()
+
+
+def fa_abi_version() -> int:
+    return int(library().fa_abi_version())
+
+
+def fa_bwd_workspace_bytes(B, H, Tq, Tk, d, dtype, grad_dtype) -> int:
+    return int(library().fa_bwd_workspace_bytes(B, H, Tq, Tk, d, dtype, grad_dtype))
+
+
+# ----------------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _check(t, name, shape, dtype=None, device=None):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fa_fwd(q, k, v, o, lse, *, scale=None, causal=False, stream=None) -> None:
+    """Launch the forward pass into caller-provided `o` [B,H,Tq,d] and `lse` [B,H,Tq] fp32."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    _check(k, "k", (B, H, Tk, d), q.dtype, dev)
+    _check(v, "v", (B, H, Tk, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), q.dtype, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, Tq, Tk, d, c, int(bool(causal)), _dtype_code(q), _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_fwd")
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, *, scale=None, causal=False, stream=None) -> None:
+    """Launch the backward pass into caller-provided dq, dk, dv (bf16 or fp32).
+
+    `workspace` is a uint8 GPU tensor of at least fa_bwd_workspace_bytes(...) bytes.
+    """
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    for name, t, T in (("k", k, Tk), ("v", v, Tk), ("o", o, Tq), ("do", do, Tq)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    _check(dq, "dq", (B, H, Tq, d), None, dev)
+    _check(dk, "dk", (B, H, Tk, d), dq.dtype, dev)
+    _check(dv, "dv", (B, H, Tk, d), dq.dtype, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk, d, c, int(bool(causal)),
+                          _dtype_code(q), _dtype_code(dq), workspace.data_ptr(), nbytes,
+                          _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_bwd")
+
+
+def forward(q, k, v, *, causal=False, scale=None, stream=None):
+    """Allocate O and lse with torch and run fa_fwd.  Returns (O, lse)."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, stream=stream)
+    return o, lse
+
+
+def backward(q, k, v, o, do, lse, *, causal=False, scale=None, grad_dtype=None, stream=None):
+    """Allocate gradients and workspace with torch and run fa_bwd.  Returns (dQ, dK, dV).
+
+    grad_dtype defaults to the input dtype (torch.float32 is also allowed for
+    bf16 inputs).
+    """
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty((B, H, Tq, d), dtype=gd, device=q.device)
+    dk = torch.empty((B, H, Tk, d), dtype=gd, device=q.device)
+    dv = torch.empty((B, H, Tk, d), dtype=gd, device=q.device)
+    nbytes = fa_bwd_workspace_bytes(B, H, Tq, Tk, d, _dtype_code(q), _dtype_code(dq))
+    if nbytes == 0:
+        raise ValueError("invalid arguments for fa_bwd")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=scale, causal=causal, stream=stream)
+    return dq, dk, dv

@@ -1,0 +1,87 @@
+// C-ABI entry points of libfa.so: argument checks, dispatch on (dtype, d), launches.
+// Every check runs before any device work; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_d(int d) { return d == 64 || d == 128 || d == 256; }
+bool valid_dtype(int t) { return t == FA_F32 || t == FA_BF16; }
+
+int check_common(int B, int H, int Tq, int Tk, int d, float scale, int dtype) {
+  if (B < 1 || H < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (!valid_d(d)) return FA_ERR_HEADDIM;
+  if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  // element offsets are 64-bit inside the kernels; guard the products anyway
+  const long long bh = (long long)B * H;
+  if (bh > (1LL << 31) || bh * (long long)(Tq > Tk ? Tq : Tk) * d > (1LL << 50)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return 1; }
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: B, H, Tq and Tk must be >= 1 and the grid must fit";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128, 256)";
+    case FA_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
+           int d, float scale, int causal, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, Tq, Tk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse)) return FA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  causal = causal ? 1 : 0;
+  if (dtype == FA_BF16) return fa::launch_fwd_bf16(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal, s);
+  return fa::launch_fwd_f32(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal, s);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, int grad_dtype) {
+  if (check_common(B, H, Tq, Tk, d, 1.f, dtype) != FA_OK || !valid_dtype(grad_dtype)) return 0;
+  const long long rows = (long long)B * H * Tq;
+  long long floats = fa::bwd_rows_padded(rows);
+  if (dtype == FA_BF16 && grad_dtype == FA_BF16) floats += rows * d;
+  return (size_t)floats * sizeof(float);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
+           void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
+           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return FA_ERR_NULL;
+  int st = check_common(B, H, Tq, Tk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!valid_dtype(grad_dtype) || (dtype == FA_F32 && grad_dtype != FA_F32)) return FA_ERR_DTYPE;
+  const size_t need = fa_bwd_workspace_bytes(B, H, Tq, Tk, d, dtype, grad_dtype);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  causal = causal ? 1 : 0;
+  if (dtype == FA_BF16)
+    return fa::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal,
+                               grad_dtype == FA_F32 ? 1 : 0, workspace, s);
+  return fa::launch_bwd_f32(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, workspace, s);
+}
+
+}  // extern "C"

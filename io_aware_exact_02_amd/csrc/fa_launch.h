@@ -1,0 +1,24 @@
+// Internal launchers shared by the C-ABI entry points (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include "fa.h"
+
+namespace fa {
+
+// Workspace layout of fa_bwd: float32 row terms D [rows] padded to a multiple of
+// 64 floats (256 bytes), then (bf16 gradients only) the float32 dQ accumulator.
+inline long long bwd_rows_padded(long long rows) { return (rows + 63) / 64 * 64; }
+
+int launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
+                    int Tk, int d, float scale, int causal, hipStream_t stream);
+int launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
+                   int Tk, int d, float scale, int causal, hipStream_t stream);
+int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                    void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                    int grad_f32, void* workspace, hipStream_t stream);
+int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                   void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                   void* workspace, hipStream_t stream);
+int launch_rowdot_bf16(const void* dO, const void* O, float* Dout, long long rows, int d, hipStream_t stream);
+
+}  // namespace fa

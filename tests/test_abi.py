@@ -1,0 +1,112 @@
+"""Host-side checks of libfa.so: it loads, exports what include/fa.h declares, and
+rejects bad arguments with the documented codes before any device work.  These
+calls never reach a kernel launch, so they run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_exact_02_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+P = 0x10000          # a fake, 16-byte aligned pointer value: never dereferenced on these paths
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (python -m io_aware_exact_02_amd.build)")
+    return fa.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(fa.EXPORTED_SYMBOLS)
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+
+
+def test_header_documents_every_status_code():
+    text = open(HEADER).read()
+    for name, val in (("FA_OK", 0), ("FA_ERR_NULL", -1), ("FA_ERR_SHAPE", -2), ("FA_ERR_HEADDIM", -3),
+                      ("FA_ERR_DTYPE", -4), ("FA_ERR_SCALE", -5), ("FA_ERR_WORKSPACE", -6),
+                      ("FA_ERR_LAUNCH", -7), ("FA_ERR_ALIGN", -8)):
+        assert re.search(rf"{name}\s*=\s*{val}\b", text), name
+
+
+def test_strerror_and_version(lib):
+    assert fa.fa_abi_version() == 1
+    msgs = {s: fa.fa_strerror(s) for s in (OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN)}
+    assert msgs[OK] == "success"
+    assert len(set(msgs.values())) == len(msgs)
+    assert "unknown" in fa.fa_strerror(12345)
+
+
+def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Tq=8, Tk=8, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, Tq, Tk, d, scale, causal, dtype, None)
+
+
+def test_fwd_argument_errors(lib):
+    assert _fwd(lib, q=None) == NULL
+    assert _fwd(lib, lse=None) == NULL
+    for bad in (dict(B=0), dict(H=0), dict(Tq=0), dict(Tk=0), dict(Tk=-3)):
+        assert _fwd(lib, **bad) == SHAPE, bad
+    for d in (0, 32, 96, 100, 512):
+        assert _fwd(lib, d=d) == HEADDIM, d
+    assert _fwd(lib, dtype=2) == DTYPE
+    assert _fwd(lib, dtype=-1) == DTYPE
+    for s in (0.0, -1.0, float("nan"), float("inf")):
+        assert _fwd(lib, scale=s) == SCALE, s
+    assert _fwd(lib, q=P + 8) == ALIGN
+    assert _fwd(lib, lse=P + 4) == ALIGN
+
+
+def test_bwd_workspace_bytes(lib):
+    B, H, Tq, Tk, d = 2, 3, 100, 70, 128
+    rows = B * H * Tq
+    pad = (rows + 63) // 64 * 64
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 4 * (pad + rows * d)
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_F32) == 4 * pad
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_F32, fa.FA_F32) == 4 * pad
+    assert fa.fa_bwd_workspace_bytes(0, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 96, fa.FA_BF16, fa.FA_BF16) == 0
+
+
+def _bwd(lib, ws=P, ws_bytes=1 << 30, B=1, H=1, Tq=8, Tk=8, d=64, scale=0.125, dtype=fa.FA_BF16,
+         gdtype=fa.FA_BF16, null_at=None):
+    ptrs = [P] * 9
+    if null_at is not None:
+        ptrs[null_at] = None
+    return lib.fa_bwd(*ptrs, B, H, Tq, Tk, d, scale, 0, dtype, gdtype, ws, ws_bytes, None)
+
+
+def test_bwd_argument_errors(lib):
+    for i in range(9):
+        assert _bwd(lib, null_at=i) == NULL, i
+    assert _bwd(lib, B=0) == SHAPE
+    assert _bwd(lib, d=48) == HEADDIM
+    assert _bwd(lib, dtype=fa.FA_F32, gdtype=fa.FA_BF16) == DTYPE
+    assert _bwd(lib, gdtype=5) == DTYPE
+    assert _bwd(lib, scale=float("nan")) == SCALE
+    assert _bwd(lib, ws=None) == WORKSPACE
+    need = fa.fa_bwd_workspace_bytes(1, 1, 8, 8, 64, fa.FA_BF16, fa.FA_BF16)
+    assert _bwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _bwd(lib, ws=P + 8, ws_bytes=need) == ALIGN
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
