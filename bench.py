@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--cpu-seconds 15]
+
+One step is the whole path over one batch: the forward pass (fa_fwd) and the
+backward pass (fa_bwd's three phases: D pre-pass, the recomputing sweep, dQ
+rounding) on the causal bf16 workload B=8, H=32, T=4096, d=128, with every input
+already resident in device memory.  FLOPs follow the pages' convention: forward
+4 B H Tq Tk d (halved when causal), backward 2.5 x forward (five tile products
+against two).  The value is total FLOPs per step / time per step.
+
+Printed: one JSON line on stdout (progress goes to stderr), with
+  roofline      the dominant kernel's algorithmic TFLOP/s (its FLOPs per launch
+                / its mean duration from HIP events recorded on the launch
+                stream over the timed steps) against the bf16 dense MFMA peak;
+                `traffic` comes from the committed rocprofv3 counter summary
+                when that summary matches the current kernel source, else null
+  cpu_baseline  the float64 NumPy oracle, fwd+bwd on a sample of heads of the
+                same workload, timed on the host cores (a reported baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak (causal, T=4096, d=128)"
+DEFAULT_WORKLOAD = "causal_bf16_b8h32_t4096_d128"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X published dense MFMA peaks
+PROFILES = os.path.join(ROOT, "profiles")
+CPU_SHARE = 16                                  # host cores per GPU on the target box
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the HIP sources; a traffic summary names the digest it was taken at."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "io_aware_exact_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt (key = value
+    lines written from two rocprofv3 --pmc runs), or None when absent or stale."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if "=" in line and not line.startswith("#"):
+            k, v = (s.strip() for s in line.split("=", 1))
+            vals[k] = v
+    if vals.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, raw, seconds: float):
+    """Time the float64 oracle's forward+backward on whole heads of the workload."""
+    from oracle import naive
+    from io_aware_exact_02_amd.inputs import as_f64
+    cores = max(1, min(CPU_SHARE, os.cpu_count() or 1))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    scale = 1.0 / math.sqrt(w.d)
+    done, t_total = 0, 0.0
+    while done < len(heads) and t_total < seconds:
+        batch = heads[done:done + cores]
+        bi, hi = [b for b, _ in batch], [h for _, h in batch]
+        q, k, v, do = (as_f64(raw[x][bi, hi], w.dtype)[None] for x in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        naive.backward(q, k, v, do, scale, w.causal, workers=cores)
+        t_total += time.perf_counter() - t0
+        done += len(batch)
+        log(f"[cpu_baseline] {done} heads in {t_total:.1f} s")
+    flops = done / (w.B * w.H) * (w.flops_fwd() + w.flops_bwd())
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 NumPy oracle, forward+backward of {done} of {w.B * w.H} (batch, head) slices of "
+                      f"the same workload (T={w.Tq}, d={w.d}, causal={w.causal}), {t_total:.1f} s on {cores} "
+                      f"threads with one BLAS thread each; FLOPs counted as for the GPU"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget (0 = skip)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+    import torch
+    import io_aware_exact_02_amd as fa
+    from io_aware_exact_02_amd.inputs import WORKLOADS, draw_workload
+
+    w = WORKLOADS[a.workload]
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] drawing inputs for {w.name}")
+    raw = draw_workload(w, with_do=True)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v, do = (up(raw[n]) for n in ("q", "k", "v", "do"))
+    B, H, Tq, Tk, d = w.B, w.H, w.Tq, w.Tk, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nws = fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa._dtype_code(q), fa._dtype_code(dq))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    phases = [fa.FA_BWD_PRE, fa.FA_BWD_MAIN, fa.FA_BWD_POST]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, stream=stream)
+        for i, ph in enumerate(phases):
+            if ev is not None:
+                ev[i + 1].record(stream)
+            fa.fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, ws, ph, causal=w.causal, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    log(f"[bench] warmup {a.warmup}")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    log(f"[bench] timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / a.steps
+    names = ["fwd", "bwd_pre", "bwd_main", "bwd_post"]
+    dur = {n: sum(events[s][i].elapsed_time(events[s][i + 1]) for s in range(a.steps)) / a.steps
+           for i, n in enumerate(names)}
+    f_fwd, f_bwd = w.flops_fwd(), w.flops_bwd()
+    total = f_fwd + f_bwd
+    value = total / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    kflops = {"fwd": f_fwd, "bwd_main": f_bwd}
+    kernels = {}
+    for n in names:
+        entry = {"ms": round(dur[n], 4)}
+        if n in kflops:
+            tf = kflops[n] / (dur[n] * 1e-3) / 1e12
+            entry.update(tflops=round(tf, 1), frac_of_peak=round(tf / peak, 4))
+        kernels[n] = entry
+    dom = max(("fwd", "bwd_main"), key=lambda n: dur[n])
+    ach = kflops[dom] / (dur[dom] * 1e-3) / 1e12
+    kernel_name = {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_bf16_kernel"}[dom]
+    roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": read_traffic(kernel_name, w.name),
+                "kernel": kernel_name}
+    cpu = None
+    if a.cpu_seconds > 0:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(w, raw, a.cpu_seconds)
+    out = {
+        "metric": METRIC if w.name == DEFAULT_WORKLOAD else f"attention fwd+bwd TFLOP/s ({w.name})",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1), see io_aware_exact_02_amd/inputs.py)",
+        "config": {"workload": f"{w.name}_fwd_bwd", "B": B, "H": H, "Tq": Tq, "Tk": Tk, "d": d,
+                   "causal": w.causal, "pass": "forward+backward"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

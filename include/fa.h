@@ -49,10 +49,19 @@ typedef enum {
   FA_ERR_SCALE = -5,      /* scale not finite or not > 0                         */
   FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than fa_bwd_workspace_bytes */
   FA_ERR_LAUNCH = -7,     /* the HIP runtime rejected a launch                   */
-  FA_ERR_ALIGN = -8       /* a device pointer is not 16-byte aligned             */
+  FA_ERR_ALIGN = -8,      /* a device pointer is not 16-byte aligned             */
+  FA_ERR_PHASE = -9       /* unknown bits in an fa_bwd_phases mask               */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Phases of the backward pass, for fa_bwd_phases. */
+typedef enum {
+  FA_BWD_PRE = 1,   /* D = rowsum(dO * O) into the workspace; clear the dQ accumulator */
+  FA_BWD_MAIN = 2,  /* the sweep: recompute P, accumulate dK, dV, add into dQ         */
+  FA_BWD_POST = 4,  /* round the float32 dQ accumulator to bf16 (bf16 gradients only) */
+  FA_BWD_ALL = 7
+} fa_bwd_phase;
 
 /*
  * Forward pass ([ZtF] "The forward pass", steps 1-3; FlashAttention-2 order:
@@ -93,6 +102,22 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            const float* lse, void* dQ, void* dK, void* dV,
            int B, int H, int Tq, int Tk, int d, float scale, int causal,
            int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same backward pass split into its phases, for callers that schedule or
+ * time them separately: `phases` is an OR of fa_bwd_phase bits, and the
+ * phases it names run in the order PRE, MAIN, POST on `stream`.  Running the
+ * three in that order (in one call or several, with the same arguments and
+ * workspace) is exactly fa_bwd.  MAIN reads what PRE left in the workspace and
+ * in dQ; POST reads what MAIN accumulated.  Same arguments and errors as
+ * fa_bwd, plus FA_ERR_PHASE for bits outside FA_BWD_ALL; phases = 0 checks the
+ * arguments and launches nothing.
+ */
+int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* lse, void* dQ, void* dK, void* dV,
+                  int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                  int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+                  int phases, void* stream);
 
 /* Static, human-readable text for an fa_status value (never NULL). */
 const char* fa_strerror(int status);

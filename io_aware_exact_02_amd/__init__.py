@@ -20,15 +20,17 @@ import math
 import os
 
 __all__ = [
-    "FA_F32", "FA_BF16", "FAError", "LIB_PATH", "library", "fa_fwd", "fa_bwd",
-    "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
+    "FA_F32", "FA_BF16", "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_POST", "FA_BWD_ALL", "FAError", "LIB_PATH", "library", "fa_fwd", "fa_bwd",
+    "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
     "EXPORTED_SYMBOLS",
 ]
 
 FA_F32 = 0
 FA_BF16 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror",
+                    "fa_abi_version")
+FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST, FA_BWD_ALL = 1, 2, 4, 7
 
 _lib = None
 
@@ -54,6 +56,8 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_phases.argtypes = lib.fa_bwd.argtypes[:-1] + [i, vp]
+    lib.fa_bwd_phases.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_strerror.argtypes = [i]
@@ -135,6 +139,13 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, *, scale=None, causal=Fal
 
     `workspace` is a uint8 GPU tensor of at least fa_bwd_workspace_bytes(...) bytes.
     """
+    fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, workspace, FA_BWD_ALL, scale=scale, causal=causal,
+                  stream=stream)
+
+
+def fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, workspace, phases, *, scale=None, causal=False,
+                  stream=None) -> None:
+    """Launch the named backward phases (an OR of FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST)."""
     torch = _torch()
     B, H, Tq, d = q.shape
     Tk = k.shape[2]
@@ -150,12 +161,12 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, *, scale=None, causal=Fal
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     c = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nbytes = workspace.numel() * workspace.element_size()
-    st = library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk, d, c, int(bool(causal)),
-                          _dtype_code(q), _dtype_code(dq), workspace.data_ptr(), nbytes,
-                          _stream_handle(stream, dev))
+    st = library().fa_bwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk, d, c,
+                                 int(bool(causal)), _dtype_code(q), _dtype_code(dq), workspace.data_ptr(), nbytes,
+                                 int(phases), _stream_handle(stream, dev))
     if st != 0:
-        raise FAError(st, "fa_bwd")
+        raise FAError(st, "fa_bwd_phases")
 
 
 def forward(q, k, v, *, causal=False, scale=None, stream=None):

@@ -40,6 +40,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    case FA_ERR_PHASE: return "unknown bits in the backward phase mask";
     default: return "unknown fa_status";
   }
 }
@@ -64,24 +65,33 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, in
   return (size_t)floats * sizeof(float);
 }
 
-int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
-           void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
-           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                  void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                  int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, int phases, void* stream) {
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return FA_ERR_NULL;
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
   if (!valid_dtype(grad_dtype) || (dtype == FA_F32 && grad_dtype != FA_F32)) return FA_ERR_DTYPE;
+  if (phases & ~FA_BWD_ALL) return FA_ERR_PHASE;
   const size_t need = fa_bwd_workspace_bytes(B, H, Tq, Tk, d, dtype, grad_dtype);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_ALIGN;
+  if (phases == 0) return FA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   causal = causal ? 1 : 0;
   if (dtype == FA_BF16)
     return fa::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal,
-                               grad_dtype == FA_F32 ? 1 : 0, workspace, s);
-  return fa::launch_bwd_f32(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, workspace, s);
+                               grad_dtype == FA_F32 ? 1 : 0, workspace, phases, s);
+  return fa::launch_bwd_f32(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, workspace, phases, s);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
+           void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
+           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, grad_dtype,
+                       workspace, workspace_bytes, FA_BWD_ALL, stream);
 }
 
 }  // extern "C"

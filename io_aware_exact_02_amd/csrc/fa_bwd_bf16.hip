@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
 template <int D>
 int bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
         void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int grad_f32, void* workspace,
-        hipStream_t stream) {
+        int phases, hipStream_t stream) {
   const long long rows = (long long)B * H * Tq;
   const long long nq = rows * D;
   const int nkb = (Tk + kBKC - 1) / kBKC;
@@ -326,21 +326,25 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
   if (nblk > 0x7fffffffLL || nfill > 0x7fffffffLL) return FA_ERR_SHAPE;
   float* Dws = static_cast<float*>(workspace);
   float* acc = grad_f32 ? static_cast<float*>(dQ) : Dws + bwd_rows_padded(rows);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc, nq);
-  int st = launch_rowdot_bf16(dO, O, Dws, rows, D, stream);
-  if (st != FA_OK) return st;
-  const float cl2e = scale * kLog2e;
-  auto q = static_cast<const uint16_t*>(Q);
-  auto k = static_cast<const uint16_t*>(K);
-  auto v = static_cast<const uint16_t*>(V);
-  auto g = static_cast<const uint16_t*>(dO);
-  if (causal)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g, lse, Dws,
-                       acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
-  else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g, lse, Dws,
-                       acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
-  if (!grad_f32)
+  if (phases & FA_BWD_PRE) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc, nq);
+    const int st = launch_rowdot_bf16(dO, O, Dws, rows, D, stream);
+    if (st != FA_OK) return st;
+  }
+  if (phases & FA_BWD_MAIN) {
+    const float cl2e = scale * kLog2e;
+    auto q = static_cast<const uint16_t*>(Q);
+    auto k = static_cast<const uint16_t*>(K);
+    auto v = static_cast<const uint16_t*>(V);
+    auto g = static_cast<const uint16_t*>(dO);
+    if (causal)
+      hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g, lse,
+                         Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+    else
+      hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g, lse,
+                         Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+  }
+  if ((phases & FA_BWD_POST) && !grad_f32)
     hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc,
                        static_cast<uint16_t*>(dQ), nq);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -350,11 +354,11 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
 
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                    int grad_f32, void* workspace, hipStream_t stream) {
+                    int grad_f32, void* workspace, int phases, hipStream_t stream) {
   switch (d) {
-    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, stream);
-    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, stream);
-    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, stream);
+    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, phases, stream);
+    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, phases, stream);
+    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, phases, stream);
     default: return FA_ERR_HEADDIM;
   }
 }

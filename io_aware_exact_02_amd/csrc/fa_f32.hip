@@ -257,14 +257,16 @@ int fwd_f32(const float* Q, const float* K, const float* V, float* O, float* lse
 template <int D>
 int bwd_f32(const float* Q, const float* K, const float* V, const float* Ov, const float* dO, const float* lse,
             float* dQ, float* dK, float* dV, int B, int H, int Tq, int Tk, float scale, int causal, float* Dws,
-            hipStream_t stream) {
+            int phases, hipStream_t stream) {
   constexpr int ROWS = 256 / (D / 16);
   const long long rows = (long long)B * H * Tq;
   const long long nrd = (rows + 15) / 16;
   const int nqb = (Tq + ROWS - 1) / ROWS, nkb = (Tk + ROWS - 1) / ROWS;
   const long long nq = (long long)nqb * B * H, nk = (long long)nkb * B * H;
   if (nrd > 0x7fffffffLL || nq > 0x7fffffffLL || nk > 0x7fffffffLL) return FA_ERR_SHAPE;
-  hipLaunchKernelGGL((rowdot_kernel<D, float>), dim3((unsigned)nrd), dim3(256), 0, stream, dO, Ov, Dws, rows);
+  if (phases & FA_BWD_PRE)
+    hipLaunchKernelGGL((rowdot_kernel<D, float>), dim3((unsigned)nrd), dim3(256), 0, stream, dO, Ov, Dws, rows);
+  if (!(phases & FA_BWD_MAIN)) return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
   if (causal) {
     hipLaunchKernelGGL((bwd_kv_f32_kernel<D, true>), dim3((unsigned)nk), dim3(256), 0, stream, Q, K, V, dO, lse, Dws,
                        dK, dV, Tq, Tk, scale, nkb);
@@ -297,7 +299,7 @@ int launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* 
 
 int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                    void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                   void* workspace, hipStream_t stream) {
+                   void* workspace, int phases, hipStream_t stream) {
   auto q = static_cast<const float*>(Q);
   auto k = static_cast<const float*>(K);
   auto v = static_cast<const float*>(V);
@@ -308,9 +310,9 @@ int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, c
   auto dv = static_cast<float*>(dV);
   auto ws = static_cast<float*>(workspace);
   switch (d) {
-    case 64: return bwd_f32<64>(q, k, v, o, g, lse, dq, dk, dv, B, H, Tq, Tk, scale, causal, ws, stream);
-    case 128: return bwd_f32<128>(q, k, v, o, g, lse, dq, dk, dv, B, H, Tq, Tk, scale, causal, ws, stream);
-    case 256: return bwd_f32<256>(q, k, v, o, g, lse, dq, dk, dv, B, H, Tq, Tk, scale, causal, ws, stream);
+    case 64: return bwd_f32<64>(q, k, v, o, g, lse, dq, dk, dv, B, H, Tq, Tk, scale, causal, ws, phases, stream);
+    case 128: return bwd_f32<128>(q, k, v, o, g, lse, dq, dk, dv, B, H, Tq, Tk, scale, causal, ws, phases, stream);
+    case 256: return bwd_f32<256>(q, k, v, o, g, lse, dq, dk, dv, B, H, Tq, Tk, scale, causal, ws, phases, stream);
     default: return FA_ERR_HEADDIM;
   }
 }

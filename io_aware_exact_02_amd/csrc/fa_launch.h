@@ -15,10 +15,10 @@ int launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* 
                    int Tk, int d, float scale, int causal, hipStream_t stream);
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                    int grad_f32, void* workspace, hipStream_t stream);
+                    int grad_f32, void* workspace, int phases, hipStream_t stream);
 int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                    void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                   void* workspace, hipStream_t stream);
+                   void* workspace, int phases, hipStream_t stream);
 int launch_rowdot_bf16(const void* dO, const void* O, float* Dout, long long rows, int d, hipStream_t stream);
 
 }  // namespace fa

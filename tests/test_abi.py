@@ -12,7 +12,7 @@ import io_aware_exact_02_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN, PHASE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 P = 0x10000          # a fake, 16-byte aligned pointer value: never dereferenced on these paths
 
 
@@ -41,13 +41,13 @@ def test_header_documents_every_status_code():
     text = open(HEADER).read()
     for name, val in (("FA_OK", 0), ("FA_ERR_NULL", -1), ("FA_ERR_SHAPE", -2), ("FA_ERR_HEADDIM", -3),
                       ("FA_ERR_DTYPE", -4), ("FA_ERR_SCALE", -5), ("FA_ERR_WORKSPACE", -6),
-                      ("FA_ERR_LAUNCH", -7), ("FA_ERR_ALIGN", -8)):
+                      ("FA_ERR_LAUNCH", -7), ("FA_ERR_ALIGN", -8), ("FA_ERR_PHASE", -9)):
         assert re.search(rf"{name}\s*=\s*{val}\b", text), name
 
 
 def test_strerror_and_version(lib):
     assert fa.fa_abi_version() == 1
-    msgs = {s: fa.fa_strerror(s) for s in (OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN)}
+    msgs = {s: fa.fa_strerror(s) for s in (OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN, PHASE)}
     assert msgs[OK] == "success"
     assert len(set(msgs.values())) == len(msgs)
     assert "unknown" in fa.fa_strerror(12345)
@@ -110,3 +110,13 @@ def test_binding_rejects_cpu_tensors(lib):
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def test_bwd_phase_mask(lib):
+    need = fa.fa_bwd_workspace_bytes(1, 1, 8, 8, 64, fa.FA_BF16, fa.FA_BF16)
+    args = [P] * 9 + [1, 1, 8, 8, 64, 0.125, 0, fa.FA_BF16, fa.FA_BF16, P, need]
+    assert lib.fa_bwd_phases(*args, 8, None) == PHASE
+    assert lib.fa_bwd_phases(*args, -1, None) == PHASE
+    assert lib.fa_bwd_phases(*args, 0, None) == OK          # checks only, launches nothing
+    bad = list(args); bad[0] = None
+    assert lib.fa_bwd_phases(*bad, 0, None) == NULL
