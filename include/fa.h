@@ -68,14 +68,17 @@ typedef enum {
  * one workgroup per query block, one sweep over the key/value blocks, O and
  * lse written once).
  *   Q [B][H][Tq][d], K and V [B][H][Tk][d]  (dtype)          in
- *   O [B][H][Tq][d] (dtype), lse [B][H][Tq] (float32)         out
- *   scale   the factor on Q K^T; the usual choice is 1/sqrt(d)
- *   causal  0 = full attention, 1 = query r sees keys l <= r
+ *   O [B][H][Tq][d] (out_dtype), lse [B][H][Tq] (float32)     out
+ *   scale      the factor on Q K^T; the usual choice is 1/sqrt(d)
+ *   causal     0 = full attention, 1 = query r sees keys l <= r
+ *   out_dtype  storage type of O: the input dtype, or FA_F32 for bf16 inputs
+ *              (keeps O's float32 accumulation unrounded, e.g. for a backward
+ *              pass whose row terms D = dO . O must not carry bf16 rounding)
  * Returns FA_OK or an fa_status error code.
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
            int B, int H, int Tq, int Tk, int d, float scale, int causal,
-           int dtype, void* stream);
+           int dtype, int out_dtype, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs: the row terms D_r = dO_r . O_r
@@ -88,10 +91,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, in
 
 /*
  * Backward pass by recomputation ([ZtF] "The backward pass, derived"):
- *   Q, K, V, O, dO (dtype), lse (float32, as written by fa_fwd)      in
- *   dQ [B][H][Tq][d], dK and dV [B][H][Tk][d] (grad_dtype)           out
- * grad_dtype: FA_BF16 or FA_F32 for bfloat16 inputs; FA_F32 for float32
- * inputs.  The dQ contributions of different key blocks are summed with
+ *   Q, K, V, dO (dtype), O (o_dtype), lse (float32, as fa_fwd wrote it)  in
+ *   dQ [B][H][Tq][d], dK and dV [B][H][Tk][d] (grad_dtype)               out
+ * o_dtype and grad_dtype: the input dtype, or FA_F32 for bfloat16 inputs.  The dQ contributions of different key blocks are summed with
  * float32 atomic additions, so dQ may differ in its last bits between runs
  * ([ZtF] "Which loop goes outside?"); dK and dV are deterministic.
  * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes,
@@ -101,7 +103,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, in
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* lse, void* dQ, void* dK, void* dV,
            int B, int H, int Tq, int Tk, int d, float scale, int causal,
-           int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+           int dtype, int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+           void* stream);
 
 /*
  * The same backward pass split into its phases, for callers that schedule or
@@ -116,7 +119,7 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
 int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                   const float* lse, void* dQ, void* dK, void* dV,
                   int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                  int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+                  int dtype, int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
                   int phases, void* stream);
 
 /* Static, human-readable text for an fa_status value (never NULL). */

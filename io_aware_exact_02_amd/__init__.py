@@ -52,9 +52,9 @@ def library() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m io_aware_exact_02_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.fa_fwd.restype = i
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp, sz, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_phases.argtypes = lib.fa_bwd.argtypes[:-1] + [i, vp]
     lib.fa_bwd_phases.restype = i
@@ -117,7 +117,9 @@ def _stream_handle(stream, device):
 
 
 def fa_fwd(q, k, v, o, lse, *, scale=None, causal=False, stream=None) -> None:
-    """Launch the forward pass into caller-provided `o` [B,H,Tq,d] and `lse` [B,H,Tq] fp32."""
+    """Launch the forward pass into caller-provided `o` [B,H,Tq,d] and `lse` [B,H,Tq] fp32.
+
+    `o` has the inputs' dtype, or float32 for bf16 inputs (O left unrounded)."""
     torch = _torch()
     B, H, Tq, d = q.shape
     Tk = k.shape[2]
@@ -125,11 +127,12 @@ def fa_fwd(q, k, v, o, lse, *, scale=None, causal=False, stream=None) -> None:
     _check(q, "q", (B, H, Tq, d), device=dev)
     _check(k, "k", (B, H, Tk, d), q.dtype, dev)
     _check(v, "v", (B, H, Tk, d), q.dtype, dev)
-    _check(o, "o", (B, H, Tq, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
     _check(lse, "lse", (B, H, Tq), torch.float32, dev)
     c = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                          B, H, Tq, Tk, d, c, int(bool(causal)), _dtype_code(q), _stream_handle(stream, dev))
+                          B, H, Tq, Tk, d, c, int(bool(causal)), _dtype_code(q), _dtype_code(o),
+                          _stream_handle(stream, dev))
     if st != 0:
         raise FAError(st, "fa_fwd")
 
@@ -151,8 +154,9 @@ def fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, workspace, phases, *, scale=N
     Tk = k.shape[2]
     dev = q.device
     _check(q, "q", (B, H, Tq, d), device=dev)
-    for name, t, T in (("k", k, Tk), ("v", v, Tk), ("o", o, Tq), ("do", do, Tq)):
+    for name, t, T in (("k", k, Tk), ("v", v, Tk), ("do", do, Tq)):
         _check(t, name, (B, H, T, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
     _check(lse, "lse", (B, H, Tq), torch.float32, dev)
     _check(dq, "dq", (B, H, Tq, d), None, dev)
     _check(dk, "dk", (B, H, Tk, d), dq.dtype, dev)
@@ -163,17 +167,20 @@ def fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, workspace, phases, *, scale=N
     nbytes = workspace.numel() * workspace.element_size()
     st = library().fa_bwd_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk, d, c,
-                                 int(bool(causal)), _dtype_code(q), _dtype_code(dq), workspace.data_ptr(), nbytes,
+                                 int(bool(causal)), _dtype_code(q), _dtype_code(o), _dtype_code(dq),
+                                 workspace.data_ptr(), nbytes,
                                  int(phases), _stream_handle(stream, dev))
     if st != 0:
         raise FAError(st, "fa_bwd_phases")
 
 
-def forward(q, k, v, *, causal=False, scale=None, stream=None):
-    """Allocate O and lse with torch and run fa_fwd.  Returns (O, lse)."""
+def forward(q, k, v, *, causal=False, scale=None, out_dtype=None, stream=None):
+    """Allocate O and lse with torch and run fa_fwd.  Returns (O, lse).
+
+    out_dtype: O's dtype (default: the inputs'; torch.float32 allowed for bf16)."""
     torch = _torch()
     B, H, Tq, d = q.shape
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, stream=stream)
     return o, lse

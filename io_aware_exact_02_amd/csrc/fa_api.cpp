@@ -18,8 +18,11 @@ int check_common(int B, int H, int Tq, int Tk, int d, float scale, int dtype) {
   if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   // element offsets are 64-bit inside the kernels; guard the products anyway
+  // one (batch, head) slice must stay below 2 GiB: the kernels address a slice
+  // with 32-bit byte offsets (buffer resources)
   const long long bh = (long long)B * H;
-  if (bh > (1LL << 31) || bh * (long long)(Tq > Tk ? Tq : Tk) * d > (1LL << 50)) return FA_ERR_SHAPE;
+  const long long tmax = Tq > Tk ? Tq : Tk;
+  if (bh > (1LL << 31) || tmax * d * 4 >= (1LL << 31)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -46,14 +49,16 @@ const char* fa_strerror(int status) {
 }
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
-           int d, float scale, int causal, int dtype, void* stream) {
+           int d, float scale, int causal, int dtype, int out_dtype, void* stream) {
   if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
+  if (!valid_dtype(out_dtype) || (dtype == FA_F32 && out_dtype != FA_F32)) return FA_ERR_DTYPE;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse)) return FA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   causal = causal ? 1 : 0;
-  if (dtype == FA_BF16) return fa::launch_fwd_bf16(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal, s);
+  if (dtype == FA_BF16)
+    return fa::launch_fwd_bf16(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal, out_dtype == FA_F32 ? 1 : 0, s);
   return fa::launch_fwd_f32(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal, s);
 }
 
@@ -67,11 +72,13 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, in
 
 int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                   void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                  int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, int phases, void* stream) {
+                  int dtype, int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes, int phases,
+                  void* stream) {
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return FA_ERR_NULL;
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
   if (!valid_dtype(grad_dtype) || (dtype == FA_F32 && grad_dtype != FA_F32)) return FA_ERR_DTYPE;
+  if (!valid_dtype(o_dtype) || (dtype == FA_F32 && o_dtype != FA_F32)) return FA_ERR_DTYPE;
   if (phases & ~FA_BWD_ALL) return FA_ERR_PHASE;
   const size_t need = fa_bwd_workspace_bytes(B, H, Tq, Tk, d, dtype, grad_dtype);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -83,15 +90,15 @@ int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, co
   causal = causal ? 1 : 0;
   if (dtype == FA_BF16)
     return fa::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal,
-                               grad_dtype == FA_F32 ? 1 : 0, workspace, phases, s);
+                               o_dtype == FA_F32 ? 1 : 0, grad_dtype == FA_F32 ? 1 : 0, workspace, phases, s);
   return fa::launch_bwd_f32(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, workspace, phases, s);
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
            void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
-           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return fa_bwd_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, grad_dtype,
-                       workspace, workspace_bytes, FA_BWD_ALL, stream);
+           int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype,
+                       grad_dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
 }
 
 }  // extern "C"

@@ -316,8 +316,8 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
 
 template <int D>
 int bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
-        void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int grad_f32, void* workspace,
-        int phases, hipStream_t stream) {
+        void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int o_f32, int grad_f32,
+        void* workspace, int phases, hipStream_t stream) {
   const long long rows = (long long)B * H * Tq;
   const long long nq = rows * D;
   const int nkb = (Tk + kBKC - 1) / kBKC;
@@ -328,7 +328,7 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
   float* acc = grad_f32 ? static_cast<float*>(dQ) : Dws + bwd_rows_padded(rows);
   if (phases & FA_BWD_PRE) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc, nq);
-    const int st = launch_rowdot_bf16(dO, O, Dws, rows, D, stream);
+    const int st = launch_rowdot_bf16(dO, O, o_f32, Dws, rows, D, stream);
     if (st != FA_OK) return st;
   }
   if (phases & FA_BWD_MAIN) {
@@ -354,11 +354,11 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
 
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                    int grad_f32, void* workspace, int phases, hipStream_t stream) {
+                    int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream) {
   switch (d) {
-    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, phases, stream);
-    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, phases, stream);
-    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, grad_f32, workspace, phases, stream);
+    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream);
+    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream);
+    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream);
     default: return FA_ERR_HEADDIM;
   }
 }

@@ -31,6 +31,17 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Buffer resource over [base, base + nbytes): loads at byte offsets at or past
+// nbytes return zeros instead of touching memory (the raw-buffer range check),
+// which replaces per-row bounds branches for ragged tails.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, unsigned byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
 
@@ -56,8 +67,22 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Low / high bf16 halves of two words, packed (word a -> low half, word b -> high half).
-__device__ __forceinline__ unsigned lo_lo(unsigned a, unsigned b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ unsigned hi_hi(unsigned a, unsigned b) { return (a >> 16) | (b & 0xffff0000u); }
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima): every vector
+// memory load issued so far has returned.  Placed where a loop iteration has
+// already consumed its loads, it tells the compiler's wait-count tracking that
+// nothing is outstanding at the back edge.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Low / high bf16 halves of two words, packed (word a -> low half, word b -> high
+// half); one v_perm_b32 each (selector bytes 0-3 pick from a, 4-7 from b).
+__device__ __forceinline__ unsigned lo_lo(unsigned a, unsigned b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ unsigned hi_hi(unsigned a, unsigned b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// acc + lo + hi of a packed bf16 pair, in float32 (v_dot2c_f32_bf16 against 1.0).
+__device__ __forceinline__ float add_bf16_pair(unsigned pair, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+
 
 }  // namespace fa

@@ -2,70 +2,93 @@
 //
 // [ZtF] = "FlashAttention", zerotofrontier.app textbook section 12.3.
 //
-// One workgroup owns a block of BR = 128 query rows of one (batch, head) and
-// makes one sweep over the key/value blocks ([ZtF] "The forward pass"); each
-// of its four waves owns 32 query rows.  Per key block of BC keys:
-//   * K_j and V_j are read from HBM with 16-byte coalesced loads into
-//     registers one block ahead, then written to a double-buffered LDS stage.
-//     V is transposed on the way (8x8 bf16 blocks in registers) so that every
-//     MFMA operand read below is one conflict-free ds_read_b128.
-//   * S^T = K_j Q_i^T on 32x32x16 bf16 MFMA with Q_i held in registers.  The
-//     transposed product puts one query row per lane (and its other half in
-//     lane ^ 32), so the row maximum and row sum are register reductions plus
-//     one v_permlane32_swap.
-//   * Masking only where a tile crosses the causal diagonal or the key tail
-//     ([ZtF] "The causal mask, and the tiles you never visit": tiles above the
-//     diagonal are never loaded -- the sweep stops at the block's last query).
-//   * P~ = exp2(S * scale*log2(e) - m) with the hardware exp2; the running sum
-//     l and output O~ are rescaled by exp2(m_old - m_new) ([ZtF] step 2.5)
-//     only when the running maximum grew by more than 8 (log2 units): between
-//     rescales both keep the same reference, so the final O~/l is unchanged
-//     and P~ stays <= 2^8.
-//   * O~^T += V_j^T P~^T on MFMA, P~ taken straight from the S registers
-//     (rounded to bf16).
-// Epilogue: O = O~/l rounded to bf16, lse = ln2 * (m + log2 l) ([ZtF] step 3).
+// One workgroup owns a block of 128 query rows of one (batch, head) and makes
+// one sweep over the key/value blocks ([ZtF] "The forward pass"); each of its
+// four waves owns 32 query rows, held as MFMA B operands in registers.
+//
+// Data movement per key block j of BC keys:
+//   * K_j goes HBM -> LDS with buffer_load ... lds (no registers, no VALU):
+//     lane l of a load lands at LDS base + 16 l, so the 16-byte chunks of a K
+//     row are placed XOR-swizzled by row, which makes the MFMA operand reads
+//     below conflict-free without padding.  Rows past Tk read as zeros.
+//   * V_j goes HBM -> registers (16-byte buffer loads) -> LDS transposed
+//     (4x8 bf16 blocks repacked in registers), so the PV product's operand is
+//     one ds_read_b128 per MFMA as well.
+// Products (32x32x16 bf16 MFMA, float32 accumulation):
+//   * S^T = K_j Q^T puts one query row per lane (its other half in lane ^ 32):
+//     the row maximum and sum are register reductions plus a v_permlane32_swap.
+//   * O~^T += V_j^T P~^T with P~ taken straight from the S registers.
+// Softmax ([ZtF] steps 2.3-2.5), in scale*log2(e) units with the hardware
+// exp2: P~ = exp2(S c - m) against a reference maximum m that is moved (and O~
+// and the sums rescaled by exp2(m_old - m_new)) only when a row's maximum has
+// grown past it by more than 8; in between, the same reference holds for
+// numerator and denominator, so the result is unchanged and P~ <= 2^8.
+// Two running sums: the unrounded one gives lse; O~ is divided by the sum of
+// the bf16-rounded weights the PV product actually used, which cancels the
+// rounding of a row's dominant weight to first order.
+// Masking only on tiles that cross the causal diagonal or the key tail; tiles
+// above the diagonal are never loaded ([ZtF] "The causal mask, and the tiles
+// you never visit": the sweep stops at the block's last query).
+//
+// One barrier per block: block j's S, softmax and PV run while K_{j+1} (into
+// the other LDS stage) and V_{j+1} (into registers) are in flight from HBM;
+// V_{j+1} is repacked into LDS at the end.  On gfx950 the MFMA and vector-ALU
+// work of a SIMD do not overlap in time (the second wave on the SIMD covers
+// latencies), so the softmax is kept to as few vector instructions per score
+// as possible.
+// Epilogue ([ZtF] step 3): O = O~/l (bf16 or float32), lse = ln2 (m + log2 l).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-template <int D> struct FwdTile;
-template <> struct FwdTile<64>  { static constexpr int BC = 128; };
-template <> struct FwdTile<128> { static constexpr int BC = 64; };
-template <> struct FwdTile<256> { static constexpr int BC = 32; };
+template <int D> struct FwdCfg;
+template <> struct FwdCfg<64>  { static constexpr int BC = 64; static constexpr int WAVES_PER_EU = 2; };
+template <> struct FwdCfg<128> { static constexpr int BC = 64; static constexpr int WAVES_PER_EU = 2; };
+template <> struct FwdCfg<256> { static constexpr int BC = 32; static constexpr int WAVES_PER_EU = 1; };
 
 constexpr int kWaves = 4;
-constexpr int kBR = 32 * kWaves;          // query rows per workgroup
-constexpr float kRescaleSlack = 8.0f;     // log2 units
+constexpr int kBR = 32 * kWaves;     // query rows per workgroup
+constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 template <int D>
 struct FwdLayout {
-  static constexpr int BC = FwdTile<D>::BC;
-  static constexpr int KSTR = D + 8;        // bf16 per K row in LDS (16 B pad)
-  static constexpr int VSTR = BC + 8;       // bf16 per V^T row in LDS (16 B pad)
-  static constexpr int KELEMS = BC * KSTR;
-  static constexpr int VELEMS = D * VSTR;
-  static constexpr int STAGE = KELEMS + VELEMS;
-  static constexpr int NKB = BC / 32;       // 32-key MFMA blocks per tile
-  static constexpr int NDB = D / 32;        // 32-wide output blocks
-  static constexpr int NDS = D / 16;        // k-steps of the QK^T product
-  // Every tile holds BC*D = 8192 elements of K and of V: 128 threads move V as
-  // 8x8 blocks, the other 128 move K as 8 chunks of 16 bytes each.
-  static_assert(BC * D == 8192, "tile loader assumes 8192-element tiles");
+  static constexpr int BC = FwdCfg<D>::BC;
+  static constexpr int NC = D / 8;                   // 16-byte chunks per K row
+  static constexpr int KST = BC * D * 2;             // bytes per K stage (unpadded, swizzled)
+  static constexpr int VSTR = BC + 8;                // bf16 per V^T row (16-byte pad)
+  static constexpr int VST = D * VSTR * 2;           // bytes per V^T stage
+  static constexpr int BYTES = 2 * KST + 2 * VST;
+  static constexpr int NKB = BC / 32;                // 32-key MFMA blocks per tile
+  static constexpr int NDB = D / 32;                 // 32-feature output blocks
+  static constexpr int NDS = D / 16;                 // k-steps of the QK^T product
+  static constexpr int KDMA = KST / 1024;            // 1 KB LDS-load instructions per K tile
+  static constexpr int KDMA_W = KDMA / kWaves;       // ... per wave
+  static constexpr int NVB = (BC / 4) * (D / 8);     // 4x8 V blocks per tile
+  static_assert(KDMA % kWaves == 0, "K tile must split evenly over the waves");
+  static_assert(NVB <= 256, "one V block per thread at most");
+  static_assert(NC == 8 || NC >= 16, "swizzle assumes 8 or >= 16 chunks per row");
+  static constexpr int k_off(int st) { return st * KST; }
+  static constexpr int v_off(int st) { return 2 * KST + st * VST; }
 };
 
-// Position of key x (0..15) of a 16-key group inside its V^T row: the middle
-// two quads are swapped so that the 8 keys one MFMA k-slot half needs
-// (quads {h, h+2}) are contiguous.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+// Chunk swizzle of K row r: with 16 or more chunks per row the 16 rows a
+// half-wave reads land on 16 distinct 16-byte bank groups; with 8 chunks
+// (128-byte rows, two per 256-byte bank cycle) rows pair up by r >> 1.
+template <int NC>
+__device__ __forceinline__ int kswz(int r) { return NC >= 16 ? (r & 15) : ((r >> 1) & 7); }
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_EU)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                     const uint16_t* __restrict__ V, void* __restrict__ O,
                      float* __restrict__ lse, int Tq, int Tk, float cl2e, int nqb) {
   using L = FwdLayout<D>;
   constexpr int BC = L::BC;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   // Workgroup -> (head, query block).  Consecutive workgroup ids go to
   // different XCDs round-robin; remapping gives each XCD a contiguous range of
@@ -84,73 +107,63 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int q0 = qb * kBR;
   const int qw = q0 + wave * 32;
   const int myq = qw + lq;
-  const bool wave_active = qw < Tq;
 
-  // Q_i fragments (B operand of S^T = K Q^T): column = query, k = features.
+  // Per-head buffer resources: rows past Tq / Tk read as zeros.
+  const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+  const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
+  const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
+
+  // Q fragments (B operand of S^T = K Q^T): column = query, k = features.
   bf16x8 qf[L::NDS];
 #pragma unroll
-  for (int ds = 0; ds < L::NDS; ++ds) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (myq < Tq) v = ld16(Q + qbase + (size_t)myq * D + ds * 16 + 8 * hf);
-    qf[ds] = as_bf16x8(v);
-  }
+  for (int ds = 0; ds < L::NDS; ++ds)
+    qf[ds] = as_bf16x8(bload16(rq, ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u));
 
   int ntile = (Tk + BC - 1) / BC;
-  if (CAUSAL) {
-    const int last_q = min(q0 + kBR, Tq) - 1;
-    ntile = min(ntile, last_q / BC + 1);
-  }
-  const int last_q_wave = min(qw + 31, Tq - 1);
+  if (CAUSAL) ntile = min(ntile, (min(q0 + kBR, Tq) - 1) / BC + 1);
 
-  // ---- global -> register staging of one K/V tile ----
-  u32x4 stg[8];
-  const bool v_loader = tid < 128;
-  const int lt = v_loader ? tid : tid - 128;
-  // V loader: 8x8 block (key group gk, feature group dg)
-  const int gk = lt % (BC / 8), dg = lt / (BC / 8);
-  const int vt = gk >> 1, vh = gk & 1;
-  auto vkey = [&](int i) { return 16 * vt + 4 * vh + (i < 4 ? i : 4 + i); };
-
-  auto gload = [&](int j) {
-    const int k0 = j * BC;
-    if (v_loader) {
+  // ---- K: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
+  auto k_dma = [&](int k0, int kst_off) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = k0 + vkey(i);
-        stg[i] = (key < Tk) ? ld16(V + kbase + (size_t)key * D + dg * 8) : (u32x4){0u, 0u, 0u, 0u};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = lt + 128 * i;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        const int key = k0 + row;
-        stg[i] = (key < Tk) ? ld16(K + kbase + (size_t)key * D + col8 * 8) : (u32x4){0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < L::KDMA_W; ++i) {
+      const int g = wave * L::KDMA_W + i;
+      const int s = g * 64 + lane;
+      const int row = s / L::NC, cp = s % L::NC;
+      const int src = cp ^ kswz<L::NC>(row);
+      const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(smem + kst_off + g * 1024), 16, off, 0, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-    uint16_t* Ks = smem + buf * L::STAGE;
-    uint16_t* Vs = Ks + L::KELEMS;
+  // Per-lane K read offset (bytes, relative to a stage and a 32-key block) for
+  // k-step ds: chunk (2 ds + hf) ^ swz of row lq.  The XOR only touches bits 5..7
+  // of kbase_lane (rows are >= 128 bytes), so each k-step is kbase_lane ^ (ds << 5).
+  const int kswz_l = kswz<L::NC>(lq);
+  const int kbase_lane = lq * D * 2 + (((kswz_l >> 1) << 5) | ((hf ^ (kswz_l & 1)) << 4));
+
+  // ---- V: HBM -> registers -> LDS transposed (4 keys x 8 features per thread).
+  const bool v_loader = tid < L::NVB;
+  const int kq = tid % (BC / 4), dg = tid / (BC / 4);
+  // position of key quad kq in its V^T row: the middle quads of each 16 keys are
+  // swapped so the 8 keys an MFMA k-slot half needs are contiguous
+  const int kq3 = kq & 3;
+  const int vpos = 16 * (kq >> 2) + 4 * (kq3 == 1 ? 2 : (kq3 == 2 ? 1 : kq3));
+  u32x4 vst[4];
+  auto v_load = [&](int k0) {
     if (v_loader) {
-      // column c of the 8x8 block -> V^T row dg*8+c, positions 16*vt + 8*vh .. +7
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vst[i] = bload16(rv, ((unsigned)(k0 + 4 * kq + i) * D + dg * 8) * 2u);
+    }
+  };
+  auto v_store = [&](int vst_off) {
+    if (v_loader) {
+      char* base = smem + vst_off + (dg * 8 * L::VSTR + vpos) * 2;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        u32x4 even, odd;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          even[p] = lo_lo(stg[2 * p][w], stg[2 * p + 1][w]);
-          odd[p] = hi_hi(stg[2 * p][w], stg[2 * p + 1][w]);
-        }
-        st16(Vs + (dg * 8 + 2 * w) * L::VSTR + 16 * vt + 8 * vh, even);
-        st16(Vs + (dg * 8 + 2 * w + 1) * L::VSTR + 16 * vt + 8 * vh, odd);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = lt + 128 * i;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        st16(Ks + row * L::KSTR + col8 * 8, stg[i]);
+        const u32x2 even = {lo_lo(vst[0][w], vst[1][w]), lo_lo(vst[2][w], vst[3][w])};
+        const u32x2 odd = {hi_hi(vst[0][w], vst[1][w]), hi_hi(vst[2][w], vst[3][w])};
+        st8(base + (2 * w) * L::VSTR * 2, even);
+        st8(base + (2 * w + 1) * L::VSTR * 2, odd);
       }
     }
   };
@@ -161,138 +174,174 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m_ref = -INFINITY;   // reference maximum, scale*log2(e) units
-  float l_part = 0.f;        // this lane's share of the running sum
+  float l_part = 0.f;        // this lane's share of the sum of the weights
+  float lr_part = 0.f;       // ... and of the bf16-rounded weights
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntile; ++j) {
-    if (j + 1 < ntile) gload(j + 1);
-    const int k0 = j * BC;
-    const bool compute = wave_active && (!CAUSAL || k0 <= last_q_wave);
-    if (compute) {
-      const uint16_t* Ks = smem + (j & 1) * L::STAGE;
-      const uint16_t* Vs = Ks + L::KELEMS;
-      // S^T = K_j Q_i^T
-      f32x16 s[L::NKB];
+  auto s_product = [&](f32x16 (&s)[L::NKB], int kst_off) {
+#pragma unroll
+    for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < L::NDS; ++ds)
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-        for (int ds = 0; ds < L::NDS; ++ds) {
-          const bf16x8 a = as_bf16x8(ld16(Ks + (kb * 32 + lq) * L::KSTR + ds * 16 + 8 * hf));
-          s[kb] = mfma32(a, qf[ds], s[kb]);
-        }
+        const bf16x8 a = as_bf16x8(ld16(smem + kst_off + kb * 32 * D * 2 + (kbase_lane ^ (ds << 5))));
+        s[kb] = mfma32(a, qf[ds], s[kb]);
       }
-      // mask: causal diagonal tiles and the key tail only
-      const bool need_mask = (CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= Tk || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
-          }
-      }
-      // row maximum of the tile
-      float mx = -INFINITY;
+  };
+  auto mask_tile = [&](f32x16 (&s)[L::NKB], int j) {
+    const int k0 = j * BC;
+    if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk)) {
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m_ref, mx * cl2e);
-      const bool grow = m_new > m_ref + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
-        const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
-        if (grow) m_ref = m_new;
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        l_part *= alpha;
-      }
-      const float mneg = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      // P~ = exp2(S * scale*log2e - m), packed to bf16 B operands
-      bf16x8 pf[L::NKB][2];
-#pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb) {
-        float p[16];
-#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(__builtin_fmaf(s[kb][r], cl2e, mneg));
-          l_part += p[r];
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= Tk || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
         }
+    }
+  };
+
+  // ---- prologue: K_0 and V_0 into LDS stage 0
+  // A block index past the sweep maps to row Tk: its loads return zeros and
+  // move no data, so the steps below need no branches around their loads.
+  auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
+  k_dma(0, L::k_off(0));
+  v_load(0);
+  v_store(L::v_off(0));
+  wait_vmem_all();
+  __syncthreads();
+
+  auto step = [&](int j, auto stage) {
+    constexpr int ST = decltype(stage)::value;        // j % 2
+    // block j+1 in flight: K straight into LDS, V into registers
+    v_load(first_row(j + 1));
+    k_dma(first_row(j + 1), L::k_off(ST ^ 1));
+    f32x16 s[L::NKB];
+    s_product(s, L::k_off(ST));
+    mask_tile(s, j);
+    float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 w;
+    for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16(p[8 * t + 2 * e], p[8 * t + 2 * e + 1]);
-          pf[kb][t] = as_bf16x8(w);
-        }
-      }
-      // O~^T += V_j^T P~^T
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = half_swap_max(mx) * cl2e;
+    const bool grow = mx > m_ref + kRescaleSlack;     // never true for a row with no visible key yet
+    if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+      const float alpha = grow ? fast_exp2(m_ref - mx) : 1.f;   // 0 on a row's first block
+      if (grow) m_ref = mx;
 #pragma unroll
       for (int db = 0; db < L::NDB; ++db)
 #pragma unroll
-        for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const bf16x8 a = as_bf16x8(ld16(Vs + (db * 32 + lq) * L::VSTR + kb * 32 + 16 * t + 8 * hf));
-            o[db] = mfma32(a, pf[kb][t], o[db]);
-          }
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l_part *= alpha;
+      lr_part *= alpha;
     }
-    if (j + 1 < ntile) lstore((j + 1) & 1);
+    const float mneg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    // P~ rounded to bf16 for the PV product; both sums updated
+    bf16x8 pf[L::NKB][2];
+    float psum = 0.f, prsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * t + 2 * e;
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], cl2e, mneg));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cl2e, mneg));
+          psum += p0 + p1;
+          w[e] = pack_bf16(p0, p1);
+          prsum = add_bf16_pair(w[e], prsum);
+        }
+        pf[kb][t] = as_bf16x8(w);
+      }
+    l_part += psum;
+    lr_part += prsum;
+    // O~^T += V_j^T P~_j^T (independent accumulators back to back)
+    const char* vs = smem + L::v_off(ST);
+#pragma unroll
+    for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) {
+          const bf16x8 a =
+              as_bf16x8(ld16(vs + ((db * 32 + lq) * L::VSTR + kb * 32 + 16 * t + 8 * hf) * 2));
+          o[db] = mfma32(a, pf[kb][t], o[db]);
+        }
+    v_store(L::v_off(ST ^ 1));
+    wait_vmem_all();
     __syncthreads();
+  };
+
+  for (int j = 0; j < ntile; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntile) step(j + 1, std::integral_constant<int, 1>{});
   }
 
-  if (!wave_active) return;
+  if (qw >= Tq) return;
   const float l_tot = half_swap_sum(l_part);
+  const float lr_tot = half_swap_sum(lr_part);
   if (myq >= Tq) return;
-  const float inv = 1.f / l_tot;
+  const float inv = 1.f / lr_tot;
 #pragma unroll
   for (int db = 0; db < L::NDB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = db * 32 + 8 * g + 4 * hf;
-      u32x2 w;
-      w[0] = pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-      w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-      st8(O + qbase + (size_t)myq * D + d0, w);
+      const size_t off = qbase + (size_t)myq * D + d0;
+      if (OUT_F32) {
+        const f32x4 w = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(O) + off) = w;
+      } else {
+        u32x2 w;
+        w[0] = pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+        w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        st8(static_cast<uint16_t*>(O) + off, w);
+      }
     }
-  if (hf == 0) lse[(size_t)bh * Tq + myq] = (m_ref + __log2f(l_tot)) * kLn2;
+  if (hf == 0) lse[(size_t)bh * Tq + myq] = (m_ref + log2f(l_tot)) * kLn2;
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
+void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
+                float* lse, int Tq, int Tk, float cl2e, int nqb) {
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32>), grid, dim3(256), 0, stream, q, k, v, o, lse, Tq, Tk,
+                     cl2e, nqb);
 }
 
 template <int D>
-int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
-           int Tk, float scale, int causal, hipStream_t stream) {
+int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
+           float scale, int causal, int out_f32, hipStream_t stream) {
   const int nqb = (Tq + kBR - 1) / kBR;
   const long long nblk = (long long)nqb * B * H;
   if (nblk > 0x7fffffffLL) return FA_ERR_SHAPE;
   const float cl2e = scale * kLog2e;
-  dim3 grid((unsigned)nblk), block(256);
+  const dim3 grid((unsigned)nblk);
   auto q = static_cast<const uint16_t*>(Q);
   auto k = static_cast<const uint16_t*>(K);
   auto v = static_cast<const uint16_t*>(V);
-  auto o = static_cast<uint16_t*>(O);
-  if (causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, block, 0, stream, q, k, v, o, lse, Tq, Tk, cl2e, nqb);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, block, 0, stream, q, k, v, o, lse, Tq, Tk, cl2e, nqb);
+  if (causal) {
+    if (out_f32) launch_one<D, true, true>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
+    else launch_one<D, true, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
+  } else {
+    if (out_f32) launch_one<D, false, true>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
+    else launch_one<D, false, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
+  }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace
 
 int launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H,
-                    int Tq, int Tk, int d, float scale, int causal, hipStream_t stream) {
+                    int Tq, int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream) {
   switch (d) {
-    case 64: return launch<64>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, stream);
-    case 128: return launch<128>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, stream);
-    case 256: return launch<256>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, stream);
+    case 64: return launch<64>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, stream);
+    case 128: return launch<128>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, stream);
+    case 256: return launch<256>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, stream);
     default: return FA_ERR_HEADDIM;
   }
 }

@@ -10,15 +10,16 @@ namespace fa {
 inline long long bwd_rows_padded(long long rows) { return (rows + 63) / 64 * 64; }
 
 int launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
-                    int Tk, int d, float scale, int causal, hipStream_t stream);
+                    int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream);
 int launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
                    int Tk, int d, float scale, int causal, hipStream_t stream);
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                    int grad_f32, void* workspace, int phases, hipStream_t stream);
+                    int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream);
 int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                    void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                    void* workspace, int phases, hipStream_t stream);
-int launch_rowdot_bf16(const void* dO, const void* O, float* Dout, long long rows, int d, hipStream_t stream);
+int launch_rowdot_bf16(const void* dO, const void* O, int o_f32, float* Dout, long long rows, int d,
+                       hipStream_t stream);
 
 }  // namespace fa

@@ -53,8 +53,10 @@ def test_strerror_and_version(lib):
     assert "unknown" in fa.fa_strerror(12345)
 
 
-def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Tq=8, Tk=8, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16):
-    return lib.fa_fwd(q, k, v, o, lse, B, H, Tq, Tk, d, scale, causal, dtype, None)
+def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Tq=8, Tk=8, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16,
+         odtype=None):
+    odtype = dtype if odtype is None else odtype
+    return lib.fa_fwd(q, k, v, o, lse, B, H, Tq, Tk, d, scale, causal, dtype, odtype, None)
 
 
 def test_fwd_argument_errors(lib):
@@ -66,6 +68,8 @@ def test_fwd_argument_errors(lib):
         assert _fwd(lib, d=d) == HEADDIM, d
     assert _fwd(lib, dtype=2) == DTYPE
     assert _fwd(lib, dtype=-1) == DTYPE
+    assert _fwd(lib, dtype=fa.FA_F32, odtype=fa.FA_BF16) == DTYPE
+    assert _fwd(lib, odtype=3) == DTYPE
     for s in (0.0, -1.0, float("nan"), float("inf")):
         assert _fwd(lib, scale=s) == SCALE, s
     assert _fwd(lib, q=P + 8) == ALIGN
@@ -84,11 +88,12 @@ def test_bwd_workspace_bytes(lib):
 
 
 def _bwd(lib, ws=P, ws_bytes=1 << 30, B=1, H=1, Tq=8, Tk=8, d=64, scale=0.125, dtype=fa.FA_BF16,
-         gdtype=fa.FA_BF16, null_at=None):
+         gdtype=fa.FA_BF16, odtype=None, null_at=None):
     ptrs = [P] * 9
     if null_at is not None:
         ptrs[null_at] = None
-    return lib.fa_bwd(*ptrs, B, H, Tq, Tk, d, scale, 0, dtype, gdtype, ws, ws_bytes, None)
+    odtype = dtype if odtype is None else odtype
+    return lib.fa_bwd(*ptrs, B, H, Tq, Tk, d, scale, 0, dtype, odtype, gdtype, ws, ws_bytes, None)
 
 
 def test_bwd_argument_errors(lib):
@@ -98,6 +103,8 @@ def test_bwd_argument_errors(lib):
     assert _bwd(lib, d=48) == HEADDIM
     assert _bwd(lib, dtype=fa.FA_F32, gdtype=fa.FA_BF16) == DTYPE
     assert _bwd(lib, gdtype=5) == DTYPE
+    assert _bwd(lib, dtype=fa.FA_F32, gdtype=fa.FA_F32, odtype=fa.FA_BF16) == DTYPE
+    assert _bwd(lib, odtype=7) == DTYPE
     assert _bwd(lib, scale=float("nan")) == SCALE
     assert _bwd(lib, ws=None) == WORKSPACE
     need = fa.fa_bwd_workspace_bytes(1, 1, 8, 8, 64, fa.FA_BF16, fa.FA_BF16)
@@ -114,7 +121,7 @@ def test_binding_rejects_cpu_tensors(lib):
 
 def test_bwd_phase_mask(lib):
     need = fa.fa_bwd_workspace_bytes(1, 1, 8, 8, 64, fa.FA_BF16, fa.FA_BF16)
-    args = [P] * 9 + [1, 1, 8, 8, 64, 0.125, 0, fa.FA_BF16, fa.FA_BF16, P, need]
+    args = [P] * 9 + [1, 1, 8, 8, 64, 0.125, 0, fa.FA_BF16, fa.FA_BF16, fa.FA_BF16, P, need]
     assert lib.fa_bwd_phases(*args, 8, None) == PHASE
     assert lib.fa_bwd_phases(*args, -1, None) == PHASE
     assert lib.fa_bwd_phases(*args, 0, None) == OK          # checks only, launches nothing

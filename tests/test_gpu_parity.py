@@ -20,21 +20,26 @@ def _oracle_fwd(f, scale, causal):
     return naive.forward(f["q"], f["k"], f["v"], scale, causal)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "bf16_outf32"])
 @pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("Tq,Tk", SHAPES)
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_parity(dtype, d, Tq, Tk, causal):
     B, H = 2, 3
+    out32 = dtype == "bf16_outf32"
+    dtype = "bf16" if out32 else dtype
     dev, f = draw(B, H, Tq, Tk, d, dtype, seed=1000 + Tq + 7 * Tk + d)
-    O, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal)
+    O, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal,
+                        out_dtype=torch().float32 if out32 else None)
+    if out32:
+        assert O.dtype == torch().float32
     torch().cuda.synchronize()
     Or, Lr = _oracle_fwd(f, 1 / math.sqrt(d), causal)
     assert maxabs(to_f64(O), Or) <= TOL_O[dtype]
     assert maxabs(to_f64(lse), Lr) <= TOL_LSE
 
 
-@pytest.mark.parametrize("dtype,grad", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+@pytest.mark.parametrize("dtype,grad", [("bf16", "bf16"), ("bf16", "f32"), ("bf16", "f32o"), ("f32", "f32")])
 @pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("Tq,Tk", [(1, 1), (17, 17), (100, 100), (300, 300), (100, 257), (257, 100)])
 @pytest.mark.parametrize("causal", [False, True])
@@ -43,8 +48,9 @@ def test_backward_parity(dtype, grad, d, Tq, Tk, causal):
     B, H = 2, 2
     dev, f = draw(B, H, Tq, Tk, d, dtype, seed=2000 + Tq + 7 * Tk + d, with_do=True)
     scale = 1 / math.sqrt(d)
-    O, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal)
-    gd = t.float32 if grad == "f32" else t.bfloat16
+    odt = t.float32 if grad == "f32o" else None          # f32o: O kept in float32 between passes
+    O, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal, out_dtype=odt)
+    gd = t.float32 if grad in ("f32", "f32o") else t.bfloat16
     dQ, dK, dV = fa.backward(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, causal=causal, grad_dtype=gd)
     t.cuda.synchronize()
     rQ, rK, rV, _, _ = naive.backward(f["q"], f["k"], f["v"], f["do"], scale, causal)
