@@ -105,6 +105,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (a known-size "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -151,6 +154,13 @@ def main(argv=None):
         if ev is not None:
             ev[4].record(stream)
 
+    if a.calib_copy_mib > 0:
+        n = a.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] warmup {a.warmup}")
     for _ in range(a.warmup):
         step()
