@@ -4,16 +4,19 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--cpu-seconds 15]
 
 One step is the whole path over one batch: the forward pass (fa_fwd) and the
-backward pass (fa_bwd's three phases: D pre-pass, the recomputing sweep, dQ
-rounding) on the causal bf16 workload B=8, H=32, T=4096, d=128, with every input
-already resident in device memory.  FLOPs follow the pages' convention: forward
-4 B H Tq Tk d (halved when causal), backward 2.5 x forward (five tile products
-against two).  The value is total FLOPs per step / time per step.
+backward pass (fa_bwd's three phases: the D pre-pass, the key-block sweep for
+dK and dV, the query-block sweep for dQ) on the causal bf16 workload B=8, H=32,
+T=4096, d=128, with every input already resident in device memory.  FLOPs
+follow the pages' convention: forward 4 B H Tq Tk d (halved when causal),
+backward 2.5 x forward (five tile products against two); the two products the
+backward sweeps form twice are not counted.  The value is total FLOPs per step
+/ time per step.
 
 Printed: one JSON line on stdout (progress goes to stderr), with
-  roofline      the dominant kernel's algorithmic TFLOP/s (its FLOPs per launch
-                / its mean duration from HIP events recorded on the launch
-                stream over the timed steps) against the bf16 dense MFMA peak;
+  roofline      the dominant kernel's algorithmic TFLOP/s (the FLOPs of the
+                tile products it forms, per launch, / its mean duration from HIP
+                events recorded on the launch stream over the timed steps)
+                against the bf16 dense MFMA peak;
                 `traffic` comes from the committed rocprofv3 counter summary
                 when that summary matches the current kernel source, else null
   cpu_baseline  the float64 NumPy oracle, fwd+bwd on a sample of heads of the
@@ -181,7 +184,13 @@ def main(argv=None):
     total = f_fwd + f_bwd
     value = total / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    kflops = {"fwd": f_fwd, "bwd_main": f_bwd}
+    # FLOPs of the tile products each kernel forms (2 d per visible pair each):
+    # the key-block sweep forms S, dP, dV, dK; the query-block sweep S, dP, dQ.
+    # The 256-wide bf16 backward forms all five in its key-block sweep.
+    fused = w.dtype == "bf16" and d == 256
+    kflops = {"fwd": f_fwd, "bwd_main": f_bwd if fused else 0.8 * f_bwd}
+    if not fused:
+        kflops["bwd_post"] = 0.6 * f_bwd
     kernels = {}
     for n in names:
         entry = {"ms": round(dur[n], 4)}
@@ -189,9 +198,10 @@ def main(argv=None):
             tf = kflops[n] / (dur[n] * 1e-3) / 1e12
             entry.update(tflops=round(tf, 1), frac_of_peak=round(tf / peak, 4))
         kernels[n] = entry
-    dom = max(("fwd", "bwd_main"), key=lambda n: dur[n])
+    dom = max(kflops, key=lambda n: dur[n])
     ach = kflops[dom] / (dur[dom] * 1e-3) / 1e12
-    kernel_name = {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_bf16_kernel"}[dom]
+    kernel_name = {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_bf16_w4_kernel" if fused else "bwd_kv_kernel",
+                   "bwd_post": "bwd_dq_kernel"}[dom]
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": read_traffic(kernel_name, w.name),
                 "kernel": kernel_name}

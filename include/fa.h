@@ -57,9 +57,12 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
 /* Phases of the backward pass, for fa_bwd_phases. */
 typedef enum {
-  FA_BWD_PRE = 1,   /* D = rowsum(dO * O) into the workspace; clear the dQ accumulator */
-  FA_BWD_MAIN = 2,  /* the sweep: recompute P, accumulate dK, dV, add into dQ         */
-  FA_BWD_POST = 4,  /* round the float32 dQ accumulator to bf16 (bf16 gradients only) */
+  FA_BWD_PRE = 1,   /* D = rowsum(dO * O) into the workspace (and, where a float32 dQ
+                       accumulator is used, clear it)                               */
+  FA_BWD_MAIN = 2,  /* key-block sweep: recompute P, write dK and dV (d = 256 with
+                       bf16 inputs: also add each block's dQ share to the accumulator) */
+  FA_BWD_POST = 4,  /* dQ: query-block sweep that recomputes P and writes dQ (d = 256
+                       with bf16 inputs: round the accumulator to the gradient dtype) */
   FA_BWD_ALL = 7
 } fa_bwd_phase;
 
@@ -82,10 +85,11 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
 
 /*
  * Bytes of device workspace fa_bwd needs: the row terms D_r = dO_r . O_r
- * ([ZtF] "The backward pass, derived", Observation 2; float32 [B][H][Tq]) and,
- * unless grad_dtype is FA_F32, a float32 dQ accumulator [B][H][Tq][d] that
- * receives the per-key-block contributions ("Which loop goes outside?").
- * Returns 0 for invalid arguments.
+ * ([ZtF] "The backward pass, derived", Observation 2; float32 [B][H][Tq],
+ * rounded up to a multiple of 64) and, for d = 256 with bf16 inputs and bf16
+ * gradients, a float32 dQ accumulator [B][H][Tq][d] that receives the
+ * per-key-block contributions ("Which loop goes outside?").  Returns 0 for
+ * invalid arguments.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, int grad_dtype);
 
@@ -93,9 +97,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, in
  * Backward pass by recomputation ([ZtF] "The backward pass, derived"):
  *   Q, K, V, dO (dtype), O (o_dtype), lse (float32, as fa_fwd wrote it)  in
  *   dQ [B][H][Tq][d], dK and dV [B][H][Tk][d] (grad_dtype)               out
- * o_dtype and grad_dtype: the input dtype, or FA_F32 for bfloat16 inputs.  The dQ contributions of different key blocks are summed with
- * float32 atomic additions, so dQ may differ in its last bits between runs
- * ([ZtF] "Which loop goes outside?"); dK and dV are deterministic.
+ * o_dtype and grad_dtype: the input dtype, or FA_F32 for bfloat16 inputs.
+ * Two sweeps ([ZtF] "Which loop goes outside?"): one over key blocks writes dK
+ * and dV, one over query blocks writes dQ; both recompute P from lse, and every
+ * output is summed in a fixed order, so results repeat bit for bit.  The one
+ * exception is d = 256 with bf16 inputs, where the key-block sweep adds its dQ
+ * shares with float32 atomics and dQ may differ in its last bits between runs.
  * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes,
  * 16-byte aligned, owned by the caller; its contents on entry do not matter.
  * Returns FA_OK or an fa_status error code.
@@ -111,8 +118,9 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
  * time them separately: `phases` is an OR of fa_bwd_phase bits, and the
  * phases it names run in the order PRE, MAIN, POST on `stream`.  Running the
  * three in that order (in one call or several, with the same arguments and
- * workspace) is exactly fa_bwd.  MAIN reads what PRE left in the workspace and
- * in dQ; POST reads what MAIN accumulated.  Same arguments and errors as
+ * workspace) is exactly fa_bwd.  MAIN and POST read the row terms PRE left in
+ * the workspace; where a dQ accumulator is used, POST reads what MAIN added to
+ * it.  Same arguments and errors as
  * fa_bwd, plus FA_ERR_PHASE for bits outside FA_BWD_ALL; phases = 0 checks the
  * arguments and launches nothing.
  */

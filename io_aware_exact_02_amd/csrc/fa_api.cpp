@@ -66,7 +66,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, in
   if (check_common(B, H, Tq, Tk, d, 1.f, dtype) != FA_OK || !valid_dtype(grad_dtype)) return 0;
   const long long rows = (long long)B * H * Tq;
   long long floats = fa::bwd_rows_padded(rows);
-  if (dtype == FA_BF16 && grad_dtype == FA_BF16) floats += rows * d;
+  // only the 256-wide bf16 backward sums dQ in a float32 accumulator (bf16 gradients)
+  if (dtype == FA_BF16 && grad_dtype == FA_BF16 && d == 256) floats += rows * d;
   return (size_t)floats * sizeof(float);
 }
 

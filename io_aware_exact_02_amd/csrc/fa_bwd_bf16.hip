@@ -3,33 +3,40 @@
 // [ZtF] = "FlashAttention", zerotofrontier.app textbook section 12.3,
 // sections "The backward pass, derived" and "Which loop goes outside?".
 //
-// One workgroup owns a block of 128 keys of one (batch, head); each of its
-// four waves owns 32 of them and keeps K_j, V_j (as MFMA B operands) and the
-// float32 accumulators dK_j, dV_j in registers for the whole sweep over query
-// blocks of 32 rows (causal: starting at the first query that can see the
-// block).  Per query block i:
+// Every kernel here starts from the row terms D = rowsum(dO * O) that a
+// pre-pass leaves in the workspace (Observation 2) and rebuilds the weights
+// from lse as P = exp2(S * scale*log2e - lse*log2e) (Observation 1).
+//
+// Head widths 64 and 128: two sweeps, no atomics, each output summed in a
+// fixed order.
+//   * bwd_kv_kernel: one workgroup per block of 128 keys sweeps the query
+//     blocks and writes dK_j and dV_j once.
+//   * bwd_dq_kernel: one workgroup per block of 256 queries sweeps the key
+//     blocks and writes dQ_i once.
+// The split costs two extra tile products (S and dP are formed in both sweeps)
+// but no dQ traffic beyond one write: adding each key block's share of dQ with
+// float32 atomics would send Tk/128 partial sums per dQ element through the
+// memory-side atomic units, which is slower on this part than recomputing.
+//
+// Head width 256 (bwd_bf16_w4_kernel): a single key-block sweep whose four
+// waves each own 32 keys and keep K_j, V_j (as MFMA B operands) and the float32
+// accumulators dK_j, dV_j in registers.  Per query block i:
 //   * Q_i and dO_i are read from HBM once (16-byte buffer loads, one block
 //     ahead, into registers) and written to LDS twice: row-major for the
 //     products that contract over the feature axis, and transposed (query
 //     order permuted to match the MFMA k-slots) for the ones that contract
 //     over queries.  lse_i (times log2 e) and D_i go to LDS as well.
-//   * S = Q_i K_j^T on MFMA with one key per lane (Observation 1: the weights
-//     are rebuilt as P = exp2(S * scale*log2e - lse*log2e)); only blocks that
-//     cross the causal diagonal are masked.  Rows past Tq and keys past Tk
-//     need no mask: their Q/dO or K/V rows read as zeros, so they add nothing.
+//   * S = Q_i K_j^T on MFMA with one key per lane; only blocks that cross the
+//     causal diagonal are masked.  Rows past Tq and keys past Tk need no mask:
+//     their Q/dO or K/V rows read as zeros, so they add nothing.
 //   * dV_j += P^T dO_i; dP = dO_i V_j^T; dS = P * (dP - D_i) (Observation 3);
 //     dK_j += dS^T Q_i -- all on MFMA with P and dS taken from registers.
-//   * dS (bf16) goes to LDS; after the block's one barrier the workgroup forms
+//   * dS (bf16) goes to LDS; after the block's barrier the workgroup forms
 //     dQ_i's contribution of all 128 keys, scale * dS K_j, and adds it to a
 //     float32 accumulator in HBM with buffer atomics (rows past Tq are dropped
 //     by the buffer range check).  The order in which different key blocks
-//     add is not fixed, so dQ's last bits may vary between runs.
-//   * Q/dO stages and the dS tile are double-buffered, so one barrier per
-//     query block orders everything (the 256-wide heads use a single stage and
-//     two barriers to stay within LDS).
-// Before the sweep, a pre-pass writes D = rowsum(dO * O) (Observation 2) and
-// clears the dQ accumulator; afterwards, if the caller wants bf16 dQ, a
-// post-pass rounds the accumulator.
+//     add is not fixed, so dQ's last bits may vary between runs.  A pre-pass
+//     clears the accumulator; a post-pass rounds it if the caller wants bf16.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -72,7 +79,7 @@ struct BwdLayout {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
-void bwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ lse, const float* __restrict__ Dr,
                      float* __restrict__ dQacc, void* __restrict__ dK, void* __restrict__ dV,
@@ -342,6 +349,496 @@ void bwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Key-block sweep for d = 64 and 128: dK_j and dV_j.
+//
+// One workgroup of eight waves per (128-key block, b, h), split by role so
+// that each SIMD holds two waves of at most 256 registers and one wave's VALU
+// or LDS waits are covered by the other's MFMA work:
+//   * score waves 0-3 (32 keys each) keep their K_j and V_j fragments in
+//     registers.  Per query tile: S = Q_i K_j^T and dP = dO_i V_j^T on MFMA,
+//     P = exp2(S c log2e - lse log2e) and dS = P * (dP - D_i) ([ZtF] "The
+//     backward pass, derived", Observations 1-3), handed on through LDS as MFMA
+//     fragments (P^T and dS^T with one key per lane).
+//   * gradient waves 4-7 (wave 4+w serves score wave w's keys) keep dV_j and
+//     dK_j in float32 registers and trail the score waves by one query tile:
+//     dV_j += P^T dO_i and dK_j += dS^T Q_i; they also stage Q_i, dO_i, lse_i and
+//     D_i two tiles ahead.
+// One barrier per phase orders everything: the row-major stages and the
+// fragment buffers alternate between two slots, the transposed Q/dO tiles
+// between three (the gradient waves read tile i-1's while writing tile i+1's).
+// Rows past Tq and keys past Tk need no masking: their Q/dO or K/V rows read as
+// zeros, so they add nothing to the gradients that are stored.
+// ---------------------------------------------------------------------------
+template <int D>
+struct KvLayout {
+  static constexpr int NSTR = D + 8;            // row-major Q_i / dO_i (bf16 per row)
+  static constexpr int TSTR = kBQ + 8;          // transposed tiles: D rows of 32 queries
+  static constexpr int N_BYTES = kBQ * NSTR * 2;
+  static constexpr int T_BYTES = D * TSTR * 2;
+  // one stage: Q_i and dO_i row-major, lse_i * log2 e, D_i
+  static constexpr int Q_N = 0;
+  static constexpr int G_N = Q_N + N_BYTES;
+  static constexpr int L_F = G_N + N_BYTES;
+  static constexpr int D_F = L_F + kBQ * 4;
+  static constexpr int STAGE = D_F + kBQ * 4;
+  static constexpr int QT_OFF = 2 * STAGE;                   // Q_i^T, three slots
+  static constexpr int GT_OFF = QT_OFF + 3 * T_BYTES;        // dO_i^T, three slots
+  static constexpr int F_WAVE = 4 * 64 * 16;                 // P^T and dS^T fragments of one score wave
+  static constexpr int F_BYTES = kWavesB * F_WAVE;
+  static constexpr int F_OFF = GT_OFF + 3 * T_BYTES;         // two slots
+  static constexpr int BYTES = F_OFF + 2 * F_BYTES;
+  static constexpr int NDS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int WPT = D / 64;                         // staging waves per tensor
+  static constexpr int SW0 = 8 - 2 * WPT;                    // first staging wave
+  static_assert(STAGE % 16 == 0 && T_BYTES % 16 == 0, "16-byte aligned regions");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_kv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dr,
+    void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e, int nkb, int grad_f32) {
+  using L = KvLayout<D>;
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+
+  const int nblk = gridDim.x, wid = blockIdx.x;
+  const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
+  const int bh = lin / nkb;
+  const int kblk = CAUSAL ? nkb - 1 - (lin % nkb) : (lin % nkb);   // causal: longest sweeps first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int wq = wave & 3;                      // key slice (score wave w and gradient wave 4+w)
+  const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
+  const int k0 = kblk * kBKC;
+  const int kw0 = k0 + wq * kKeysPerWave;
+  const int mykey = kw0 + l32;
+
+  const int nqt = (Tq + kBQ - 1) / kBQ;
+  const int it0 = CAUSAL ? min(k0 / kBQ, nqt) : 0;
+  const int n = nqt - it0;                      // query tiles in the sweep
+
+  if (wave < 4) {
+    // ============================ score waves ============================
+    const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
+    const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
+    bf16x8 kf[L::NDS], vf[L::NDS];
+#pragma unroll
+    for (int ds = 0; ds < L::NDS; ++ds) {
+      const unsigned off = ((unsigned)mykey * D + ds * 16 + 8 * hf) * 2u;
+      kf[ds] = as_bf16x8(bload16(rk, off));
+      vf[ds] = as_bf16x8(bload16(rv, off));
+    }
+    __syncthreads();
+
+    for (int s = 0; s < n; ++s) {
+      const int r0 = (it0 + s) * kBQ;
+      const char* sb_ = smem + (s & 1) * L::STAGE;
+      // S = Q_i K_j^T and dP = dO_i V_j^T: lane = key, register r = query 8(r/4)+4hf+r%4
+      f32x16 sacc, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int ds = 0; ds < L::NDS; ++ds) {
+        const bf16x8 a = as_bf16x8(ld16(sb_ + L::Q_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
+        sacc = mfma32(a, kf[ds], sacc);
+        const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
+        dp = mfma32(g, vf[ds], dp);
+      }
+      const float* lsv = reinterpret_cast<const float*>(sb_ + L::L_F);
+      const float* dsv_ = reinterpret_cast<const float*>(sb_ + L::D_F);
+      float p[16], dsv[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qr = 8 * g4 + 4 * hf;
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lsv + qr);
+        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(dsv_ + qr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          p[r] = fast_exp2(__builtin_fmaf(sacc[r], cl2e, -lv[e]));
+          dsv[r] = dp[r] - dv4[e];
+        }
+      }
+      if (CAUSAL && r0 < kw0 + kKeysPerWave - 1) {     // the tile crosses this wave's diagonal
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
+      }
+      // fragments for the gradient wave: [P^T t=0, P^T t=1, dS^T t=0, dS^T t=1], 1 KiB each
+      char* fb = smem + L::F_OFF + (s & 1) * L::F_BYTES + wq * L::F_WAVE + lane * 16;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * t + 2 * e;
+          a[e] = pack_bf16(p[r], p[r + 1]);
+          b[e] = pack_bf16(p[r] * dsv[r], p[r + 1] * dsv[r + 1]);
+        }
+        st16(fb + t * 1024, a);
+        st16(fb + (2 + t) * 1024, b);
+      }
+      __syncthreads();
+    }
+  } else {
+    // =========================== gradient waves ==========================
+    const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+    const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
+    const rsrc_t rl = make_rsrc(lse + (size_t)bh * Tq, (unsigned)Tq * 4u);
+    const rsrc_t rd = make_rsrc(Dr + (size_t)bh * Tq, (unsigned)Tq * 4u);
+
+    // Staging: WPT waves per tensor (Q, then dO); lane = 4 consecutive query rows
+    // (quad qa) x 8 features (group fg), quads fastest across lanes.  The last
+    // wave's low 32 lanes also fetch lse and D.  A tile index past the sweep maps
+    // to row Tq, whose loads return zeros.
+    const bool stager = wave >= L::SW0;
+    const bool is_g = wave >= L::SW0 + L::WPT;
+    const int sidx = ((wave - L::SW0) % L::WPT) * 64 + lane;
+    const int qa = sidx & 7, fg = sidx >> 3;
+    const rsrc_t rsrc = is_g ? rg : rq;
+    // transposed position of the quad: the middle quads of each 16 queries are
+    // swapped, matching the query order of a fragment's MFMA k-slots
+    const int tpos = 16 * (qa >> 2) + 4 * (((qa & 1) << 1) | ((qa >> 1) & 1));
+    const bool sloader = wave == 7 && lane < kBQ;
+    u32x4 stg[4];
+    float sl = 0.f, sd = 0.f;
+    auto first_row = [&](int s) { return it0 + s < nqt ? (it0 + s) * kBQ : Tq; };
+    auto gload = [&](int s) {
+      const int r0 = first_row(s);
+      if (stager) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stg[i] = bload16(rsrc, ((unsigned)(r0 + 4 * qa + i) * D + fg * 8) * 2u);
+      }
+      if (sloader) {
+        sl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (r0 + lane) * 4, 0, 0));
+        sd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (r0 + lane) * 4, 0, 0));
+      }
+    };
+    auto lstore = [&](int s) {
+      char* base = smem + (s & 1) * L::STAGE;
+      if (stager) {
+        char* N = base + (is_g ? L::G_N : L::Q_N);
+        char* T = smem + (is_g ? L::GT_OFF : L::QT_OFF) + (s % 3) * L::T_BYTES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st16(N + ((4 * qa + i) * L::NSTR + fg * 8) * 2, stg[i]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const u32x2 ev = {lo_lo(stg[0][w], stg[1][w]), lo_lo(stg[2][w], stg[3][w])};
+          const u32x2 od = {hi_hi(stg[0][w], stg[1][w]), hi_hi(stg[2][w], stg[3][w])};
+          st8(T + ((fg * 8 + 2 * w) * L::TSTR + tpos) * 2, ev);
+          st8(T + ((fg * 8 + 2 * w + 1) * L::TSTR + tpos) * 2, od);
+        }
+      }
+      if (sloader) {
+        reinterpret_cast<float*>(base + L::L_F)[lane] = sl * kLog2e;
+        reinterpret_cast<float*>(base + L::D_F)[lane] = sd;
+      }
+    };
+
+    f32x16 dk[L::NDB], dv[L::NDB];
+#pragma unroll
+    for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[db][r] = 0.f;
+        dv[db][r] = 0.f;
+      }
+
+    // dV_j += P^T dO_i and dK_j += dS^T Q_i for tile s: lane = feature column,
+    // register = key row
+    auto grad_step = [&](int s) {
+      const char* fb = smem + L::F_OFF + (s & 1) * L::F_BYTES + wq * L::F_WAVE + lane * 16;
+      const char* gt = smem + L::GT_OFF + (s % 3) * L::T_BYTES;
+      const char* qt = smem + L::QT_OFF + (s % 3) * L::T_BYTES;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pb = as_bf16x8(ld16(fb + t * 1024));
+        const bf16x8 sbf = as_bf16x8(ld16(fb + (2 + t) * 1024));
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) {
+          const int toff = ((db * 32 + l32) * L::TSTR + 16 * t + 8 * hf) * 2;
+          dv[db] = mfma32(pb, as_bf16x8(ld16(gt + toff)), dv[db]);
+          dk[db] = mfma32(sbf, as_bf16x8(ld16(qt + toff)), dk[db]);
+        }
+      }
+    };
+
+    if (n > 0) {
+      gload(0);
+      lstore(0);
+      if (n > 1) gload(1);
+    }
+    __syncthreads();
+    for (int p = 0; p < n; ++p) {
+      if (p + 1 < n) lstore(p + 1);
+      if (p + 2 < n) gload(p + 2);
+      if (p >= 1) grad_step(p - 1);
+      __syncthreads();
+    }
+    if (n > 0) grad_step(n - 1);
+
+    // dK_j = scale * dS^T Q and dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
+    const unsigned gsz = grad_f32 ? 4u : 2u;
+    const rsrc_t rdk = make_rsrc(static_cast<char*>(dK) + kbase * gsz, (unsigned)Tk * D * gsz);
+    const rsrc_t rdv = make_rsrc(static_cast<char*>(dV) + kbase * gsz, (unsigned)Tk * D * gsz);
+#pragma unroll
+    for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const unsigned idx = (unsigned)(kw0 + 8 * (r >> 2) + 4 * hf + (r & 3)) * D + db * 32 + l32;
+        const float gk = scale * dk[db][r];
+        const float gv = dv[db][r];   // a scalar copy: bit-casting a vector element in place reads element 0
+        if (grad_f32) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gk), rdk, idx * 4u, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gv), rdv, idx * 4u, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(gk, 0.f) & 0xffffu), rdk, idx * 2u, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(gv, 0.f) & 0xffffu), rdv, idx * 2u, 0, 0);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query-block sweep for d = 64 and 128: dQ_i, in the other loop order ([ZtF]
+// "Which loop goes outside?"), so that each dQ row is summed in registers by
+// one wave and written once, with no atomics and a fixed summation order.
+//
+// One workgroup of eight waves per (256-query block, b, h); each wave owns 32
+// query rows and keeps their Q and dO fragments (MFMA B operands), lse, D and
+// the float32 dQ^T accumulator in registers for a sweep over key blocks of 64
+// (causal: up to the block's last query; tiles a wave cannot see are skipped
+// by that wave).  Per key block j:
+//   * K_j and V_j go HBM -> LDS by buffer_load ... lds (rows XOR-swizzled by
+//     16-byte chunk); K_j^T goes HBM -> registers -> LDS transposed, its key
+//     order matching the k-slot order of the dS fragments below.
+//   * S^T = K_j Q^T and dP^T = V_j dO^T on MFMA put one query per lane, so lse
+//     and D are per-lane constants: P^T = exp2(S^T c log2e - lse log2e) and
+//     dS^T = P^T * (dP^T - D) ([ZtF] "The backward pass, derived").
+//   * dQ^T += K_j^T dS^T with dS^T rounded to bf16 straight from registers.
+// Epilogue: dQ = scale * dQ~, once, in the gradient dtype.
+// ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;
+constexpr int kDqBR = 32 * kDqWaves;          // query rows per workgroup
+constexpr int kDqBC = 64;                     // keys per block
+
+template <int D>
+struct DqLayout {
+  static constexpr int BC = kDqBC;
+  static constexpr int NC = D / 8;                     // 16-byte chunks per K/V row
+  static constexpr int KST = BC * D * 2;               // K (or V) tile, swizzled rows, unpadded
+  static constexpr int TSTR = BC + 8;                  // bf16 per K^T row (16-byte pad)
+  static constexpr int TST = D * TSTR * 2;
+  static constexpr int STAGE = 2 * KST + TST;
+  static constexpr int BYTES = 2 * STAGE;
+  static constexpr int NKB = BC / 32;
+  static constexpr int NDB = D / 32;
+  static constexpr int NDS = D / 16;
+  static constexpr int KDMA = KST / 1024;              // 1 KiB DMA instructions per K (or V) tile
+  static constexpr int KDMA_W = 2 * KDMA / kDqWaves;   // per wave: waves 0-3 load K, 4-7 load V
+  static constexpr int NTB = (BC / 4) * (D / 8);       // 4 keys x 8 features blocks of K^T
+  static_assert((2 * KDMA) % kDqWaves == 0 && KDMA % (kDqWaves / 2) == 0, "DMA split over the waves");
+  static_assert(NTB <= 64 * kDqWaves, "one K^T block per thread at most");
+  static_assert(NC == 8 || NC >= 16, "swizzle assumes 8 or >= 16 chunks per row");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+  static constexpr int k_off(int st) { return st * STAGE; }
+  static constexpr int v_off(int st) { return st * STAGE + KST; }
+  static constexpr int t_off(int st) { return st * STAGE + 2 * KST; }
+};
+
+// Chunk swizzle of row r of a K/V tile: with 16 or more chunks per row the 16
+// rows a half-wave reads land on 16 distinct 16-byte bank groups; with 8 chunks
+// (128-byte rows, two per 256-byte bank cycle) rows pair up by r >> 1.
+template <int NC>
+__device__ __forceinline__ int dq_swz(int r) { return NC >= 16 ? (r & 15) : ((r >> 1) & 7); }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dr,
+    void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32) {
+  using L = DqLayout<D>;
+  constexpr int BC = L::BC;
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+
+  const int nblk = gridDim.x, wid = blockIdx.x;
+  const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
+  const int bh = lin / nqb;
+  const int qb = CAUSAL ? nqb - 1 - (lin % nqb) : (lin % nqb);    // causal: longest sweeps first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
+  const int q0 = qb * kDqBR;
+  const int qw = q0 + wave * 32;
+  const int myq = qw + lq;
+
+  const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+  const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
+  const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
+  const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
+  const rsrc_t rl = make_rsrc(lse + (size_t)bh * Tq, (unsigned)Tq * 4u);
+  const rsrc_t rd = make_rsrc(Dr + (size_t)bh * Tq, (unsigned)Tq * 4u);
+
+  // Q and dO fragments (B operands): column = query, k = features
+  bf16x8 qf[L::NDS], gf[L::NDS];
+#pragma unroll
+  for (int ds = 0; ds < L::NDS; ++ds) {
+    const unsigned off = ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u;
+    qf[ds] = as_bf16x8(bload16(rq, off));
+    gf[ds] = as_bf16x8(bload16(rg, off));
+  }
+  const float lse2 = kLog2e * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0));
+  const float dq_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
+
+  int ntile = (Tk + BC - 1) / BC;
+  if (CAUSAL) ntile = min(ntile, (min(q0 + kDqBR, Tq) - 1) / BC + 1);
+
+  // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled
+  const rsrc_t rkv = wave < kDqWaves / 2 ? rk : rv;
+  auto kv_dma = [&](int k0, int st) {
+#pragma unroll
+    for (int i = 0; i < L::KDMA_W; ++i) {
+      const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
+      const int s = (g % L::KDMA) * 64 + lane;
+      const int row = s / L::NC, cp = s % L::NC;
+      const unsigned off = ((unsigned)(k0 + row) * D + (cp ^ dq_swz<L::NC>(row)) * 8) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rkv, (__attribute__((address_space(3))) void*)(smem + L::k_off(st) + g * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
+  const int swz_l = dq_swz<L::NC>(lq);
+  const int kbase_lane = lq * D * 2 + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
+
+  // ---- K^T: HBM -> registers -> LDS transposed (4 keys x 8 features per thread)
+  const bool t_loader = tid < L::NTB;
+  const int kq = tid % (BC / 4), dg = tid / (BC / 4);
+  const int kq3 = kq & 3;
+  const int tpos = 16 * (kq >> 2) + 4 * (kq3 == 1 ? 2 : (kq3 == 2 ? 1 : kq3));
+  u32x4 tst[4];
+  auto t_load = [&](int k0) {
+    if (t_loader) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tst[i] = bload16(rk, ((unsigned)(k0 + 4 * kq + i) * D + dg * 8) * 2u);
+    }
+  };
+  auto t_store = [&](int st) {
+    if (t_loader) {
+      char* base = smem + L::t_off(st) + (dg * 8 * L::TSTR + tpos) * 2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x2 even = {lo_lo(tst[0][w], tst[1][w]), lo_lo(tst[2][w], tst[3][w])};
+        const u32x2 odd = {hi_hi(tst[0][w], tst[1][w]), hi_hi(tst[2][w], tst[3][w])};
+        st8(base + (2 * w) * L::TSTR * 2, even);
+        st8(base + (2 * w + 1) * L::TSTR * 2, odd);
+      }
+    }
+  };
+
+  f32x16 dq[L::NDB];
+#pragma unroll
+  for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+
+  auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
+  kv_dma(0, 0);
+  t_load(0);
+  t_store(0);
+  wait_vmem_all();
+  __syncthreads();
+
+  auto step = [&](int j, auto stage) {
+    constexpr int ST = decltype(stage)::value;        // j % 2
+    t_load(first_row(j + 1));
+    kv_dma(first_row(j + 1), ST ^ 1);
+    const int kt0 = j * BC;
+    if (!CAUSAL || kt0 <= qw + 31) {                  // some key of the block is visible to this wave
+      const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk);
+#pragma unroll
+      for (int kb = 0; kb < L::NKB; ++kb) {
+        // S^T and dP^T for 32 keys: register r = key kt0 + 32 kb + 8(r/4)+4hf+r%4, lane = query
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = 0.f;
+          dp[r] = 0.f;
+        }
+#pragma unroll
+        for (int ds = 0; ds < L::NDS; ++ds) {
+          const int off = kb * 32 * D * 2 + (kbase_lane ^ (ds << 5));
+          s = mfma32(as_bf16x8(ld16(smem + L::k_off(ST) + off)), qf[ds], s);
+          dp = mfma32(as_bf16x8(ld16(smem + L::v_off(ST) + off)), gf[ds], dp);
+        }
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, -lse2));
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= Tk || (CAUSAL && key > myq)) p[r] = 0.f;
+          }
+        }
+        bf16x8 sf[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * t + 2 * e;
+            w[e] = pack_bf16(p[r] * (dp[r] - dq_d), p[r + 1] * (dp[r + 1] - dq_d));
+          }
+          sf[t] = as_bf16x8(w);
+        }
+        // dQ^T += K_j^T dS^T: lane = query column, register = feature row
+        const char* ts = smem + L::t_off(ST);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) {
+            const bf16x8 a = as_bf16x8(ld16(ts + ((db * 32 + lq) * L::TSTR + kb * 32 + 16 * t + 8 * hf) * 2));
+            dq[db] = mfma32(a, sf[t], dq[db]);
+          }
+      }
+    }
+    t_store(ST ^ 1);
+    wait_vmem_all();
+    __syncthreads();
+  };
+
+  for (int j = 0; j < ntile; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntile) step(j + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (myq >= Tq) return;
+  // dQ: lane = query, register 4g+e of block db = feature db*32 + 8g + 4hf + e
+#pragma unroll
+  for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + 8 * g + 4 * hf;
+      const size_t off = qbase + (size_t)myq * D + d0;
+      const float v0 = scale * dq[db][4 * g], v1 = scale * dq[db][4 * g + 1];
+      const float v2 = scale * dq[db][4 * g + 2], v3 = scale * dq[db][4 * g + 3];
+      if (grad_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(dQ) + off) = (f32x4){v0, v1, v2, v3};
+      } else {
+        const u32x2 w = {pack_bf16(v0, v1), pack_bf16(v2, v3)};
+        st8(static_cast<uint16_t*>(dQ) + off, w);
+      }
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, long long n) {
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i + 3 < n) {
@@ -372,30 +869,57 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
   const int nkb = (Tk + kBKC - 1) / kBKC;
   const long long nblk = (long long)nkb * B * H;
   const long long nfill = (nq + 1023) / 1024;
-  if (nblk > 0x7fffffffLL || nfill > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const int nqb = (Tq + kDqBR - 1) / kDqBR;
+  const long long nqblk = (long long)nqb * B * H;
+  if (nblk > 0x7fffffffLL || nfill > 0x7fffffffLL || nqblk > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const float cl2e = scale * kLog2e;
+  auto q = static_cast<const uint16_t*>(Q);
+  auto k = static_cast<const uint16_t*>(K);
+  auto v = static_cast<const uint16_t*>(V);
+  auto g = static_cast<const uint16_t*>(dO);
   float* Dws = static_cast<float*>(workspace);
-  float* acc = grad_f32 ? static_cast<float*>(dQ) : Dws + bwd_rows_padded(rows);
-  if (phases & FA_BWD_PRE) {
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc, nq);
-    const int st = launch_rowdot_bf16(dO, O, o_f32, Dws, rows, D, stream);
-    if (st != FA_OK) return st;
+  if constexpr (D == 256) {
+    // one key-block sweep that also adds dQ contributions into a float32 accumulator
+    float* acc = grad_f32 ? static_cast<float*>(dQ) : Dws + bwd_rows_padded(rows);
+    if (phases & FA_BWD_PRE) {
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc, nq);
+      const int st = launch_rowdot_bf16(dO, O, o_f32, Dws, rows, D, stream);
+      if (st != FA_OK) return st;
+    }
+    if (phases & FA_BWD_MAIN) {
+      if (causal)
+        hipLaunchKernelGGL((bwd_bf16_w4_kernel<D, true>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g,
+                           lse, Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+      else
+        hipLaunchKernelGGL((bwd_bf16_w4_kernel<D, false>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g,
+                           lse, Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+    }
+    if ((phases & FA_BWD_POST) && !grad_f32)
+      hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc,
+                         static_cast<uint16_t*>(dQ), nq);
+  } else {
+    // key-block sweep for dK, dV; query-block sweep for dQ
+    if (phases & FA_BWD_PRE) {
+      const int st = launch_rowdot_bf16(dO, O, o_f32, Dws, rows, D, stream);
+      if (st != FA_OK) return st;
+    }
+    if (phases & FA_BWD_MAIN) {
+      if (causal)
+        hipLaunchKernelGGL((bwd_kv_kernel<D, true>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, lse,
+                           Dws, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+      else
+        hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, lse,
+                           Dws, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+    }
+    if (phases & FA_BWD_POST) {
+      if (causal)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, lse,
+                           Dws, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, lse,
+                           Dws, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
+    }
   }
-  if (phases & FA_BWD_MAIN) {
-    const float cl2e = scale * kLog2e;
-    auto q = static_cast<const uint16_t*>(Q);
-    auto k = static_cast<const uint16_t*>(K);
-    auto v = static_cast<const uint16_t*>(V);
-    auto g = static_cast<const uint16_t*>(dO);
-    if (causal)
-      hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g, lse,
-                         Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
-    else
-      hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g, lse,
-                         Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
-  }
-  if ((phases & FA_BWD_POST) && !grad_f32)
-    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc,
-                       static_cast<uint16_t*>(dQ), nq);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -266,17 +266,21 @@ int bwd_f32(const float* Q, const float* K, const float* V, const float* Ov, con
   if (nrd > 0x7fffffffLL || nq > 0x7fffffffLL || nk > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (phases & FA_BWD_PRE)
     hipLaunchKernelGGL((rowdot_kernel<D, float, float>), dim3((unsigned)nrd), dim3(256), 0, stream, dO, Ov, Dws, rows);
-  if (!(phases & FA_BWD_MAIN)) return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-  if (causal) {
-    hipLaunchKernelGGL((bwd_kv_f32_kernel<D, true>), dim3((unsigned)nk), dim3(256), 0, stream, Q, K, V, dO, lse, Dws,
-                       dK, dV, Tq, Tk, scale, nkb);
-    hipLaunchKernelGGL((bwd_q_f32_kernel<D, true>), dim3((unsigned)nq), dim3(256), 0, stream, Q, K, V, dO, lse, Dws,
-                       dQ, Tq, Tk, scale, nqb);
-  } else {
-    hipLaunchKernelGGL((bwd_kv_f32_kernel<D, false>), dim3((unsigned)nk), dim3(256), 0, stream, Q, K, V, dO, lse,
-                       Dws, dK, dV, Tq, Tk, scale, nkb);
-    hipLaunchKernelGGL((bwd_q_f32_kernel<D, false>), dim3((unsigned)nq), dim3(256), 0, stream, Q, K, V, dO, lse, Dws,
-                       dQ, Tq, Tk, scale, nqb);
+  if (phases & FA_BWD_MAIN) {   // key-block sweep: dK, dV
+    if (causal)
+      hipLaunchKernelGGL((bwd_kv_f32_kernel<D, true>), dim3((unsigned)nk), dim3(256), 0, stream, Q, K, V, dO, lse,
+                         Dws, dK, dV, Tq, Tk, scale, nkb);
+    else
+      hipLaunchKernelGGL((bwd_kv_f32_kernel<D, false>), dim3((unsigned)nk), dim3(256), 0, stream, Q, K, V, dO, lse,
+                         Dws, dK, dV, Tq, Tk, scale, nkb);
+  }
+  if (phases & FA_BWD_POST) {   // query-block sweep: dQ
+    if (causal)
+      hipLaunchKernelGGL((bwd_q_f32_kernel<D, true>), dim3((unsigned)nq), dim3(256), 0, stream, Q, K, V, dO, lse,
+                         Dws, dQ, Tq, Tk, scale, nqb);
+    else
+      hipLaunchKernelGGL((bwd_q_f32_kernel<D, false>), dim3((unsigned)nq), dim3(256), 0, stream, Q, K, V, dO, lse,
+                         Dws, dQ, Tq, Tk, scale, nqb);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -80,7 +80,10 @@ def test_bwd_workspace_bytes(lib):
     B, H, Tq, Tk, d = 2, 3, 100, 70, 128
     rows = B * H * Tq
     pad = (rows + 63) // 64 * 64
-    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 4 * (pad + rows * d)
+    # row terms only; the float32 dQ accumulator exists for 256-wide bf16 heads with bf16 gradients
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 4 * pad
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 256, fa.FA_BF16, fa.FA_BF16) == 4 * (pad + rows * 256)
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 256, fa.FA_BF16, fa.FA_F32) == 4 * pad
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_F32) == 4 * pad
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_F32, fa.FA_F32) == 4 * pad
     assert fa.fa_bwd_workspace_bytes(0, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 0
