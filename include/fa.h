@@ -57,8 +57,8 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
 /* Phases of the backward pass, for fa_bwd_phases. */
 typedef enum {
-  FA_BWD_PRE = 1,   /* D = rowsum(dO * O) into the workspace (and, where a float32 dQ
-                       accumulator is used, clear it)                               */
+  FA_BWD_PRE = 1,   /* row terms D = rowsum(dO * O) (and -lse log2 e) into the
+                       workspace; where a float32 dQ accumulator is used, clear it  */
   FA_BWD_MAIN = 2,  /* key-block sweep: recompute P, write dK and dV (d = 256 with
                        bf16 inputs: also add each block's dQ share to the accumulator) */
   FA_BWD_POST = 4,  /* dQ: query-block sweep that recomputes P and writes dQ (d = 256
@@ -84,12 +84,13 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
            int dtype, int out_dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: the row terms D_r = dO_r . O_r
- * ([ZtF] "The backward pass, derived", Observation 2; float32 [B][H][Tq],
- * rounded up to a multiple of 64) and, for d = 256 with bf16 inputs and bf16
- * gradients, a float32 dQ accumulator [B][H][Tq][d] that receives the
- * per-key-block contributions ("Which loop goes outside?").  Returns 0 for
- * invalid arguments.
+ * Bytes of device workspace fa_bwd needs, all float32 and per query row
+ * ([B][H][Tq], each array rounded up to a multiple of 64 entries): the row
+ * terms D_r = dO_r . O_r ([ZtF] "The backward pass, derived", Observation 2)
+ * -- for bf16 inputs with d <= 128 stored as -D_r next to -lse_r log2(e) --
+ * and, for d = 256 with bf16 inputs and bf16 gradients, a float32 dQ
+ * accumulator [B][H][Tq][d] that receives the per-key-block contributions
+ * ("Which loop goes outside?").  Returns 0 for invalid arguments.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, int grad_dtype);
 

@@ -350,25 +350,76 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Row terms for the two sweeps below, stored negated so that they enter the
+// sweeps without a subtraction: Dn_r = -(dO_r . O_r) ([ZtF] "The backward
+// pass, derived", Observation 2) seeds the dP accumulator, so the MFMA returns
+// dP - D directly; Ln_r = -lse_r log2 e is the addend of P's exponent.
+// ---------------------------------------------------------------------------
+template <int D, bool O_F32>
+__global__ __launch_bounds__(256) void row_terms_kernel(const uint16_t* __restrict__ dO, const void* __restrict__ O,
+                                                        const float* __restrict__ lse, float* __restrict__ Dn,
+                                                        float* __restrict__ Ln, long long rows) {
+  constexpr int G = D / 8;                 // lanes per row, 8 elements each
+  constexpr int RPB = 256 / G;             // rows per block
+  const long long r = (long long)blockIdx.x * RPB + threadIdx.x / G;
+  const int j = threadIdx.x % G;
+  float part = 0.f;
+  if (r < rows) {
+    const u32x4 g = ld16(dO + r * D + 8 * j);
+    float o[8];
+    if (O_F32) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(O) + r * D + 8 * j);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(O) + r * D + 8 * j + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = a[e];
+        o[4 + e] = b[e];
+      }
+    } else {
+      const u32x4 w = ld16(static_cast<const uint16_t*>(O) + r * D + 8 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+        o[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      part = __builtin_fmaf(__builtin_bit_cast(float, g[e] << 16), o[2 * e], part);
+      part = __builtin_fmaf(__builtin_bit_cast(float, g[e] & 0xffff0000u), o[2 * e + 1], part);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) part += __shfl_xor(part, m, 64);
+  if (r < rows && j == 0) {
+    Dn[r] = -part;
+    Ln[r] = -kLog2e * lse[r];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Key-block sweep for d = 64 and 128: dK_j and dV_j.
 //
 // One workgroup of eight waves per (128-key block, b, h), split by role so
 // that each SIMD holds two waves of at most 256 registers and one wave's VALU
 // or LDS waits are covered by the other's MFMA work:
 //   * score waves 0-3 (32 keys each) keep their K_j and V_j fragments in
-//     registers.  Per query tile: S = Q_i K_j^T and dP = dO_i V_j^T on MFMA,
-//     P = exp2(S c log2e - lse log2e) and dS = P * (dP - D_i) ([ZtF] "The
-//     backward pass, derived", Observations 1-3), handed on through LDS as MFMA
-//     fragments (P^T and dS^T with one key per lane).
+//     registers.  Per query tile: S = Q_i K_j^T and dP - D = dO_i V_j^T - D_i
+//     on MFMA (the accumulator starts at -D), P = exp2(S c log2e - lse log2e)
+//     and dS = P * (dP - D) ([ZtF] "The backward pass, derived", Observations
+//     1-3), handed on through LDS as MFMA fragments (P^T and dS^T, one key per
+//     lane).  lse and D of the next tile are fetched from HBM into registers
+//     while the current tile is processed.
 //   * gradient waves 4-7 (wave 4+w serves score wave w's keys) keep dV_j and
 //     dK_j in float32 registers and trail the score waves by one query tile:
-//     dV_j += P^T dO_i and dK_j += dS^T Q_i; they also stage Q_i, dO_i, lse_i and
-//     D_i two tiles ahead.
+//     dV_j += P^T dO_i and dK_j += dS^T Q_i; they also stage Q_i and dO_i two
+//     tiles ahead.
 // One barrier per phase orders everything: the row-major stages and the
 // fragment buffers alternate between two slots, the transposed Q/dO tiles
-// between three (the gradient waves read tile i-1's while writing tile i+1's).
-// Rows past Tq and keys past Tk need no masking: their Q/dO or K/V rows read as
-// zeros, so they add nothing to the gradients that are stored.
+// between three (the gradient waves read tile i-1's while writing tile i+1's);
+// the loops are unrolled so that every slot is a constant offset.
+// Rows past Tq and keys past Tk need no masking: their Q/dO or K/V rows read
+// as zeros, so they add nothing to the gradients that are stored.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvLayout {
@@ -376,12 +427,9 @@ struct KvLayout {
   static constexpr int TSTR = kBQ + 8;          // transposed tiles: D rows of 32 queries
   static constexpr int N_BYTES = kBQ * NSTR * 2;
   static constexpr int T_BYTES = D * TSTR * 2;
-  // one stage: Q_i and dO_i row-major, lse_i * log2 e, D_i
-  static constexpr int Q_N = 0;
+  static constexpr int Q_N = 0;                              // one stage: Q_i and dO_i row-major
   static constexpr int G_N = Q_N + N_BYTES;
-  static constexpr int L_F = G_N + N_BYTES;
-  static constexpr int D_F = L_F + kBQ * 4;
-  static constexpr int STAGE = D_F + kBQ * 4;
+  static constexpr int STAGE = G_N + N_BYTES;
   static constexpr int QT_OFF = 2 * STAGE;                   // Q_i^T, three slots
   static constexpr int GT_OFF = QT_OFF + 3 * T_BYTES;        // dO_i^T, three slots
   static constexpr int F_WAVE = 4 * 64 * 16;                 // P^T and dS^T fragments of one score wave
@@ -399,7 +447,7 @@ struct KvLayout {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dr,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
     void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e, int nkb, int grad_f32) {
   using L = KvLayout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
@@ -420,11 +468,14 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   const int nqt = (Tq + kBQ - 1) / kBQ;
   const int it0 = CAUSAL ? min(k0 / kBQ, nqt) : 0;
   const int n = nqt - it0;                      // query tiles in the sweep
+  auto first_row = [&](int s) { return it0 + s < nqt ? (it0 + s) * kBQ : Tq; };
 
   if (wave < 4) {
     // ============================ score waves ============================
     const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
     const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
+    const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
+    const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
     bf16x8 kf[L::NDS], vf[L::NDS];
 #pragma unroll
     for (int ds = 0; ds < L::NDS; ++ds) {
@@ -432,18 +483,35 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       kf[ds] = as_bf16x8(bload16(rk, off));
       vf[ds] = as_bf16x8(bload16(rv, off));
     }
+    // -lse log2e and -D of the tile's queries in the accumulator order:
+    // register r <-> query 8(r/4) + 4hf + r%4 (all lanes of a half alike)
+    auto terms_load = [&](int s, f32x16& lt, f32x16& dt) {
+      const int r0 = first_row(s);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const unsigned off = (unsigned)(r0 + 8 * g4 + 4 * hf) * 4u;
+        const f32x4 a = __builtin_bit_cast(f32x4, bload16(rl, off));
+        const f32x4 b = __builtin_bit_cast(f32x4, bload16(rd, off));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lt[4 * g4 + e] = a[e];
+          dt[4 * g4 + e] = b[e];
+        }
+      }
+    };
+    f32x16 lt0, dt0, lt1, dt1;
+    terms_load(0, lt0, dt0);
     __syncthreads();
 
-    for (int s = 0; s < n; ++s) {
+    auto score_step = [&](int s, auto stage, const f32x16& lt, const f32x16& dt, f32x16& lt_n, f32x16& dt_n) {
+      constexpr int ST = decltype(stage)::value;      // s % 2
+      terms_load(s + 1, lt_n, dt_n);
       const int r0 = (it0 + s) * kBQ;
-      const char* sb_ = smem + (s & 1) * L::STAGE;
-      // S = Q_i K_j^T and dP = dO_i V_j^T: lane = key, register r = query 8(r/4)+4hf+r%4
-      f32x16 sacc, dp;
+      const char* sb_ = smem + ST * L::STAGE;
+      // S = Q_i K_j^T and dP - D = dO_i V_j^T - D_i: lane = key, register r = query 8(r/4)+4hf+r%4
+      f32x16 sacc, dp = dt;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[r] = 0.f;
-        dp[r] = 0.f;
-      }
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < L::NDS; ++ds) {
         const bf16x8 a = as_bf16x8(ld16(sb_ + L::Q_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
@@ -451,28 +519,16 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
         dp = mfma32(g, vf[ds], dp);
       }
-      const float* lsv = reinterpret_cast<const float*>(sb_ + L::L_F);
-      const float* dsv_ = reinterpret_cast<const float*>(sb_ + L::D_F);
-      float p[16], dsv[16];
+      float p[16];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qr = 8 * g4 + 4 * hf;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(lsv + qr);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(dsv_ + qr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          p[r] = fast_exp2(__builtin_fmaf(sacc[r], cl2e, -lv[e]));
-          dsv[r] = dp[r] - dv4[e];
-        }
-      }
+      for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sacc[r], cl2e, lt[r]));
       if (CAUSAL && r0 < kw0 + kKeysPerWave - 1) {     // the tile crosses this wave's diagonal
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
       }
       // fragments for the gradient wave: [P^T t=0, P^T t=1, dS^T t=0, dS^T t=1], 1 KiB each
-      char* fb = smem + L::F_OFF + (s & 1) * L::F_BYTES + wq * L::F_WAVE + lane * 16;
+      char* fb = smem + L::F_OFF + ST * L::F_BYTES + wq * L::F_WAVE + lane * 16;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         u32x4 a, b;
@@ -480,24 +536,25 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * t + 2 * e;
           a[e] = pack_bf16(p[r], p[r + 1]);
-          b[e] = pack_bf16(p[r] * dsv[r], p[r + 1] * dsv[r + 1]);
+          b[e] = pack_bf16(p[r] * dp[r], p[r + 1] * dp[r + 1]);
         }
         st16(fb + t * 1024, a);
         st16(fb + (2 + t) * 1024, b);
       }
       __syncthreads();
+    };
+    for (int s = 0; s < n; s += 2) {
+      score_step(s, std::integral_constant<int, 0>{}, lt0, dt0, lt1, dt1);
+      if (s + 1 < n) score_step(s + 1, std::integral_constant<int, 1>{}, lt1, dt1, lt0, dt0);
     }
   } else {
     // =========================== gradient waves ==========================
     const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
     const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
-    const rsrc_t rl = make_rsrc(lse + (size_t)bh * Tq, (unsigned)Tq * 4u);
-    const rsrc_t rd = make_rsrc(Dr + (size_t)bh * Tq, (unsigned)Tq * 4u);
 
     // Staging: WPT waves per tensor (Q, then dO); lane = 4 consecutive query rows
-    // (quad qa) x 8 features (group fg), quads fastest across lanes.  The last
-    // wave's low 32 lanes also fetch lse and D.  A tile index past the sweep maps
-    // to row Tq, whose loads return zeros.
+    // (quad qa) x 8 features (group fg), quads fastest across lanes.  A tile
+    // index past the sweep maps to row Tq, whose loads return zeros.
     const bool stager = wave >= L::SW0;
     const bool is_g = wave >= L::SW0 + L::WPT;
     const int sidx = ((wave - L::SW0) % L::WPT) * 64 + lane;
@@ -506,39 +563,29 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     // transposed position of the quad: the middle quads of each 16 queries are
     // swapped, matching the query order of a fragment's MFMA k-slots
     const int tpos = 16 * (qa >> 2) + 4 * (((qa & 1) << 1) | ((qa >> 1) & 1));
-    const bool sloader = wave == 7 && lane < kBQ;
+    const int n_off = (is_g ? L::G_N : L::Q_N) + ((4 * qa) * L::NSTR + fg * 8) * 2;
+    const int t_off = (is_g ? L::GT_OFF : L::QT_OFF) + ((fg * 8) * L::TSTR + tpos) * 2;
     u32x4 stg[4];
-    float sl = 0.f, sd = 0.f;
-    auto first_row = [&](int s) { return it0 + s < nqt ? (it0 + s) * kBQ : Tq; };
     auto gload = [&](int s) {
-      const int r0 = first_row(s);
       if (stager) {
+        const int r0 = first_row(s);
 #pragma unroll
         for (int i = 0; i < 4; ++i) stg[i] = bload16(rsrc, ((unsigned)(r0 + 4 * qa + i) * D + fg * 8) * 2u);
       }
-      if (sloader) {
-        sl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (r0 + lane) * 4, 0, 0));
-        sd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (r0 + lane) * 4, 0, 0));
-      }
     };
-    auto lstore = [&](int s) {
-      char* base = smem + (s & 1) * L::STAGE;
+    auto lstore = [&](int slot2, int slot3) {     // slots s % 2 and s % 3 of the tile staged
       if (stager) {
-        char* N = base + (is_g ? L::G_N : L::Q_N);
-        char* T = smem + (is_g ? L::GT_OFF : L::QT_OFF) + (s % 3) * L::T_BYTES;
+        char* N = smem + slot2 * L::STAGE + n_off;
+        char* T = smem + slot3 * L::T_BYTES + t_off;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st16(N + ((4 * qa + i) * L::NSTR + fg * 8) * 2, stg[i]);
+        for (int i = 0; i < 4; ++i) st16(N + i * L::NSTR * 2, stg[i]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const u32x2 ev = {lo_lo(stg[0][w], stg[1][w]), lo_lo(stg[2][w], stg[3][w])};
           const u32x2 od = {hi_hi(stg[0][w], stg[1][w]), hi_hi(stg[2][w], stg[3][w])};
-          st8(T + ((fg * 8 + 2 * w) * L::TSTR + tpos) * 2, ev);
-          st8(T + ((fg * 8 + 2 * w + 1) * L::TSTR + tpos) * 2, od);
+          st8(T + (2 * w) * L::TSTR * 2, ev);
+          st8(T + (2 * w + 1) * L::TSTR * 2, od);
         }
-      }
-      if (sloader) {
-        reinterpret_cast<float*>(base + L::L_F)[lane] = sl * kLog2e;
-        reinterpret_cast<float*>(base + L::D_F)[lane] = sd;
       }
     };
 
@@ -550,20 +597,22 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         dk[db][r] = 0.f;
         dv[db][r] = 0.f;
       }
+    const int f_lane = L::F_OFF + wq * L::F_WAVE + lane * 16;
+    const int t_lane = (l32 * L::TSTR + 8 * hf) * 2;
 
-    // dV_j += P^T dO_i and dK_j += dS^T Q_i for tile s: lane = feature column,
-    // register = key row
-    auto grad_step = [&](int s) {
-      const char* fb = smem + L::F_OFF + (s & 1) * L::F_BYTES + wq * L::F_WAVE + lane * 16;
-      const char* gt = smem + L::GT_OFF + (s % 3) * L::T_BYTES;
-      const char* qt = smem + L::QT_OFF + (s % 3) * L::T_BYTES;
+    // dV_j += P^T dO_i and dK_j += dS^T Q_i for the tile in slots (slot2, slot3):
+    // lane = feature column, register = key row
+    auto grad_step = [&](int slot2, int slot3) {
+      const char* fb = smem + slot2 * L::F_BYTES + f_lane;
+      const char* gt = smem + L::GT_OFF + slot3 * L::T_BYTES + t_lane;
+      const char* qt = smem + L::QT_OFF + slot3 * L::T_BYTES + t_lane;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 pb = as_bf16x8(ld16(fb + t * 1024));
         const bf16x8 sbf = as_bf16x8(ld16(fb + (2 + t) * 1024));
 #pragma unroll
         for (int db = 0; db < L::NDB; ++db) {
-          const int toff = ((db * 32 + l32) * L::TSTR + 16 * t + 8 * hf) * 2;
+          const int toff = (db * 32 * L::TSTR + 16 * t) * 2;
           dv[db] = mfma32(pb, as_bf16x8(ld16(gt + toff)), dv[db]);
           dk[db] = mfma32(sbf, as_bf16x8(ld16(qt + toff)), dk[db]);
         }
@@ -572,17 +621,25 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 
     if (n > 0) {
       gload(0);
-      lstore(0);
+      lstore(0, 0);
       if (n > 1) gload(1);
     }
     __syncthreads();
+    // phase p: gradients of tile p-1, stage tile p+1, fetch tile p+2.  m2 = p % 2
+    // and m3 = p % 3 (wave-uniform counters) pick the slots.
+    int m2 = 0, m3 = 0;
     for (int p = 0; p < n; ++p) {
-      if (p + 1 < n) lstore(p + 1);
+      const int up3 = m3 == 2 ? 0 : m3 + 1;          // (p + 1) % 3
+      const int dn3 = m3 == 0 ? 2 : m3 - 1;          // (p - 1) % 3
+      if (p >= 1) grad_step(m2 ^ 1, dn3);
+      if (p + 1 < n) lstore(m2 ^ 1, up3);
       if (p + 2 < n) gload(p + 2);
-      if (p >= 1) grad_step(p - 1);
       __syncthreads();
+      m2 ^= 1;
+      m3 = up3;
     }
-    if (n > 0) grad_step(n - 1);
+    // the last tile's gradients: its slots are ((n-1) % 2, (n-1) % 3)
+    if (n > 0) grad_step(m2 ^ 1, m3 == 0 ? 2 : m3 - 1);
 
     // dK_j = scale * dS^T Q and dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
     const unsigned gsz = grad_f32 ? 4u : 2u;
@@ -619,9 +676,10 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 //   * K_j and V_j go HBM -> LDS by buffer_load ... lds (rows XOR-swizzled by
 //     16-byte chunk); K_j^T goes HBM -> registers -> LDS transposed, its key
 //     order matching the k-slot order of the dS fragments below.
-//   * S^T = K_j Q^T and dP^T = V_j dO^T on MFMA put one query per lane, so lse
-//     and D are per-lane constants: P^T = exp2(S^T c log2e - lse log2e) and
-//     dS^T = P^T * (dP^T - D) ([ZtF] "The backward pass, derived").
+//   * S^T = K_j Q^T and dP^T - D = V_j dO^T - D on MFMA put one query per lane,
+//     so lse and D are per-lane constants (-D seeds the accumulator):
+//     P^T = exp2(S^T c log2e - lse log2e) and dS^T = P^T * (dP^T - D) ([ZtF]
+//     "The backward pass, derived").
 //   * dQ^T += K_j^T dS^T with dS^T rounded to bf16 straight from registers.
 // Epilogue: dQ = scale * dQ~, once, in the gradient dtype.
 // ---------------------------------------------------------------------------
@@ -662,7 +720,7 @@ __device__ __forceinline__ int dq_swz(int r) { return NC >= 16 ? (r & 15) : ((r 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dr,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
     void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32) {
   using L = DqLayout<D>;
   constexpr int BC = L::BC;
@@ -684,8 +742,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
   const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
   const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
-  const rsrc_t rl = make_rsrc(lse + (size_t)bh * Tq, (unsigned)Tq * 4u);
-  const rsrc_t rd = make_rsrc(Dr + (size_t)bh * Tq, (unsigned)Tq * 4u);
+  const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
+  const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
 
   // Q and dO fragments (B operands): column = query, k = features
   bf16x8 qf[L::NDS], gf[L::NDS];
@@ -695,8 +753,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     qf[ds] = as_bf16x8(bload16(rq, off));
     gf[ds] = as_bf16x8(bload16(rg, off));
   }
-  const float lse2 = kLog2e * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0));
-  const float dq_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
+  // -lse log2e and -D of this lane's query; -D seeds every dP^T accumulator
+  const float lnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0));
+  const float dnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
+  f32x16 dseed;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dseed[r] = dnq;
 
   int ntile = (Tk + BC - 1) / BC;
   if (CAUSAL) ntile = min(ntile, (min(q0 + kDqBR, Tq) - 1) / BC + 1);
@@ -765,13 +827,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
       const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk);
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb) {
-        // S^T and dP^T for 32 keys: register r = key kt0 + 32 kb + 8(r/4)+4hf+r%4, lane = query
-        f32x16 s, dp;
+        // S^T and dP^T - D for 32 keys: register r = key kt0 + 32 kb + 8(r/4)+4hf+r%4, lane = query
+        f32x16 s, dp = dseed;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
         for (int ds = 0; ds < L::NDS; ++ds) {
           const int off = kb * 32 * D * 2 + (kbase_lane ^ (ds << 5));
@@ -780,7 +839,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
         }
         float p[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, -lse2));
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, lnq));
         if (edge) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -795,7 +854,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 8 * t + 2 * e;
-            w[e] = pack_bf16(p[r] * (dp[r] - dq_d), p[r + 1] * (dp[r + 1] - dq_d));
+            w[e] = pack_bf16(p[r] * dp[r], p[r + 1] * dp[r + 1]);
           }
           sf[t] = as_bf16x8(w);
         }
@@ -898,26 +957,36 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
       hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc,
                          static_cast<uint16_t*>(dQ), nq);
   } else {
-    // key-block sweep for dK, dV; query-block sweep for dQ
+    // key-block sweep for dK, dV; query-block sweep for dQ; both read the
+    // negated row terms Dn (workspace start) and Ln (after it)
+    float* Dn = Dws;
+    float* Ln = Dws + bwd_rows_padded(rows);
     if (phases & FA_BWD_PRE) {
-      const int st = launch_rowdot_bf16(dO, O, o_f32, Dws, rows, D, stream);
-      if (st != FA_OK) return st;
+      constexpr int RPB = 256 / (D / 8);
+      const long long nrb = (rows + RPB - 1) / RPB;
+      if (nrb > 0x7fffffffLL) return FA_ERR_SHAPE;
+      if (o_f32)
+        hipLaunchKernelGGL((row_terms_kernel<D, true>), dim3((unsigned)nrb), dim3(256), 0, stream, g, O, lse, Dn, Ln,
+                           rows);
+      else
+        hipLaunchKernelGGL((row_terms_kernel<D, false>), dim3((unsigned)nrb), dim3(256), 0, stream, g, O, lse, Dn, Ln,
+                           rows);
     }
     if (phases & FA_BWD_MAIN) {
       if (causal)
-        hipLaunchKernelGGL((bwd_kv_kernel<D, true>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, lse,
-                           Dws, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+        hipLaunchKernelGGL((bwd_kv_kernel<D, true>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, Ln, Dn,
+                           dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
       else
-        hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, lse,
-                           Dws, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+        hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, Ln,
+                           Dn, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
     }
     if (phases & FA_BWD_POST) {
       if (causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, lse,
-                           Dws, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, Ln,
+                           Dn, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
       else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, lse,
-                           Dws, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, Ln,
+                           Dn, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
     }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

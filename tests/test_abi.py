@@ -80,11 +80,12 @@ def test_bwd_workspace_bytes(lib):
     B, H, Tq, Tk, d = 2, 3, 100, 70, 128
     rows = B * H * Tq
     pad = (rows + 63) // 64 * 64
-    # row terms only; the float32 dQ accumulator exists for 256-wide bf16 heads with bf16 gradients
-    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 4 * pad
+    # bf16, d <= 128: two row-term arrays (-D and -lse log2 e); d = 256: D, plus the float32 dQ
+    # accumulator when the gradients are bf16; float32 inputs: D
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 8 * pad
+    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_F32) == 8 * pad
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 256, fa.FA_BF16, fa.FA_BF16) == 4 * (pad + rows * 256)
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 256, fa.FA_BF16, fa.FA_F32) == 4 * pad
-    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_F32) == 4 * pad
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_F32, fa.FA_F32) == 4 * pad
     assert fa.fa_bwd_workspace_bytes(0, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 96, fa.FA_BF16, fa.FA_BF16) == 0
