@@ -512,13 +512,18 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       f32x16 sacc, dp = dt;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      bf16x8 qa[L::NDS], ga[L::NDS];
 #pragma unroll
       for (int ds = 0; ds < L::NDS; ++ds) {
-        const bf16x8 a = as_bf16x8(ld16(sb_ + L::Q_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
-        sacc = mfma32(a, kf[ds], sacc);
-        const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
-        dp = mfma32(g, vf[ds], dp);
+        qa[ds] = as_bf16x8(ld16(sb_ + L::Q_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
+        ga[ds] = as_bf16x8(ld16(sb_ + L::G_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
       }
+#pragma unroll
+      for (int ds = 0; ds < L::NDS; ++ds) {
+        sacc = mfma32(qa[ds], kf[ds], sacc);
+        dp = mfma32(ga[ds], vf[ds], dp);
+      }
+      sched_reads_ahead<2 * L::NDS>();
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sacc[r], cl2e, lt[r]));
@@ -606,17 +611,26 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       const char* fb = smem + slot2 * L::F_BYTES + f_lane;
       const char* gt = smem + L::GT_OFF + slot3 * L::T_BYTES + t_lane;
       const char* qt = smem + L::QT_OFF + slot3 * L::T_BYTES + t_lane;
+      bf16x8 pb[2], sbf[2], ga[2][L::NDB], qa[2][L::NDB];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 pb = as_bf16x8(ld16(fb + t * 1024));
-        const bf16x8 sbf = as_bf16x8(ld16(fb + (2 + t) * 1024));
+        pb[t] = as_bf16x8(ld16(fb + t * 1024));
+        sbf[t] = as_bf16x8(ld16(fb + (2 + t) * 1024));
 #pragma unroll
         for (int db = 0; db < L::NDB; ++db) {
           const int toff = (db * 32 * L::TSTR + 16 * t) * 2;
-          dv[db] = mfma32(pb, as_bf16x8(ld16(gt + toff)), dv[db]);
-          dk[db] = mfma32(sbf, as_bf16x8(ld16(qt + toff)), dk[db]);
+          ga[t][db] = as_bf16x8(ld16(gt + toff));
+          qa[t][db] = as_bf16x8(ld16(qt + toff));
         }
       }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) {
+          dv[db] = mfma32(pb[t], ga[t][db], dv[db]);
+          dk[db] = mfma32(sbf[t], qa[t][db], dk[db]);
+        }
+      sched_reads_ahead<4 * L::NDB, 4 * L::NDB + 4>();
     };
 
     if (n > 0) {
@@ -831,12 +845,19 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
         f32x16 s, dp = dseed;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        bf16x8 ka[L::NDS], va[L::NDS];
 #pragma unroll
         for (int ds = 0; ds < L::NDS; ++ds) {
           const int off = kb * 32 * D * 2 + (kbase_lane ^ (ds << 5));
-          s = mfma32(as_bf16x8(ld16(smem + L::k_off(ST) + off)), qf[ds], s);
-          dp = mfma32(as_bf16x8(ld16(smem + L::v_off(ST) + off)), gf[ds], dp);
+          ka[ds] = as_bf16x8(ld16(smem + L::k_off(ST) + off));
+          va[ds] = as_bf16x8(ld16(smem + L::v_off(ST) + off));
         }
+#pragma unroll
+        for (int ds = 0; ds < L::NDS; ++ds) {
+          s = mfma32(ka[ds], qf[ds], s);
+          dp = mfma32(va[ds], gf[ds], dp);
+        }
+        sched_reads_ahead<2 * L::NDS>();
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, lnq));
@@ -860,13 +881,17 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
         }
         // dQ^T += K_j^T dS^T: lane = query column, register = feature row
         const char* ts = smem + L::t_off(ST);
+        bf16x8 ta[2][L::NDB];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int db = 0; db < L::NDB; ++db) {
-            const bf16x8 a = as_bf16x8(ld16(ts + ((db * 32 + lq) * L::TSTR + kb * 32 + 16 * t + 8 * hf) * 2));
-            dq[db] = mfma32(a, sf[t], dq[db]);
-          }
+          for (int db = 0; db < L::NDB; ++db)
+            ta[t][db] = as_bf16x8(ld16(ts + ((db * 32 + lq) * L::TSTR + kb * 32 + 16 * t + 8 * hf) * 2));
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) dq[db] = mfma32(ta[t][db], sf[t], dq[db]);
+        if constexpr (2 * L::NDB >= 6) sched_reads_ahead<2 * L::NDB>();
       }
     }
     t_store(ST ^ 1);

@@ -84,5 +84,21 @@ __device__ __forceinline__ float add_bf16_pair(unsigned pair, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
 }
 
+// Scheduling hint for a block of LDS operand reads feeding MFMAs, written
+// reads-first: keep the first reads six MFMAs ahead, then issue one read per
+// MFMA.  Without it the scheduler issues each read just before its MFMA, so
+// every MFMA pair waits out a full LDS round trip.
+// With R reads and M MFMAs (R >= M) the first R - M + 6 reads go ahead.
+template <int M, int R = M>
+__device__ __forceinline__ void sched_reads_ahead() {
+  static_assert(M >= 6 && R >= M, "at least six MFMAs, no fewer reads than MFMAs");
+  __builtin_amdgcn_sched_group_barrier(0x100, R - M + 6, 0);   // DS reads
+#pragma unroll
+  for (int i = 0; i < M - 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+}
 
 }  // namespace fa

@@ -182,13 +182,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    bf16x8 ka[L::NDS][L::NKB];
 #pragma unroll
     for (int ds = 0; ds < L::NDS; ++ds)
 #pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb) {
-        const bf16x8 a = as_bf16x8(ld16(smem + kst_off + kb * 32 * D * 2 + (kbase_lane ^ (ds << 5))));
-        s[kb] = mfma32(a, qf[ds], s[kb]);
-      }
+      for (int kb = 0; kb < L::NKB; ++kb)
+        ka[ds][kb] = as_bf16x8(ld16(smem + kst_off + kb * 32 * D * 2 + (kbase_lane ^ (ds << 5))));
+#pragma unroll
+    for (int ds = 0; ds < L::NDS; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < L::NKB; ++kb) s[kb] = mfma32(ka[ds][kb], qf[ds], s[kb]);
+    sched_reads_ahead<L::NDS * L::NKB>();
   };
   auto mask_tile = [&](f32x16 (&s)[L::NKB], int j) {
     const int k0 = j * BC;
@@ -221,11 +225,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     f32x16 s[L::NKB];
     s_product(s, L::k_off(ST));
     mask_tile(s, j);
-    float mx = -INFINITY;
+    // row maximum and (below) row sums as shallow trees of independent partial
+    // results: long chains of dependent vector ops leave the wave stalled
+    float mq[4];
 #pragma unroll
-    for (int kb = 0; kb < L::NKB; ++kb)
+    for (int q = 0; q < 4; ++q) mq[q] = fmaxf(fmaxf(s[0][4 * q], s[0][4 * q + 1]), fmaxf(s[0][4 * q + 2], s[0][4 * q + 3]));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int kb = 1; kb < L::NKB; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mq[q] = fmaxf(mq[q], fmaxf(fmaxf(s[kb][4 * q], s[kb][4 * q + 1]), fmaxf(s[kb][4 * q + 2], s[kb][4 * q + 3])));
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = half_swap_max(mx) * cl2e;
     const bool grow = mx > m_ref + kRescaleSlack;     // never true for a row with no visible key yet
     if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
@@ -241,7 +251,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const float mneg = (m_ref == -INFINITY) ? 0.f : -m_ref;
     // P~ rounded to bf16 for the PV product; both sums updated
     bf16x8 pf[L::NKB][2];
-    float psum = 0.f, prsum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f}, prs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
@@ -252,26 +262,31 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           const int r = 8 * t + 2 * e;
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], cl2e, mneg));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cl2e, mneg));
-          psum += p0 + p1;
+          ps[e] += p0 + p1;
           w[e] = pack_bf16(p0, p1);
-          prsum = add_bf16_pair(w[e], prsum);
+          prs[e] = add_bf16_pair(w[e], prs[e]);
         }
         pf[kb][t] = as_bf16x8(w);
       }
-    l_part += psum;
-    lr_part += prsum;
+    l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
     // O~^T += V_j^T P~_j^T (independent accumulators back to back)
     const char* vs = smem + L::v_off(ST);
+    bf16x8 va[L::NKB][2][L::NDB];
 #pragma unroll
     for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int db = 0; db < L::NDB; ++db) {
-          const bf16x8 a =
-              as_bf16x8(ld16(vs + ((db * 32 + lq) * L::VSTR + kb * 32 + 16 * t + 8 * hf) * 2));
-          o[db] = mfma32(a, pf[kb][t], o[db]);
-        }
+        for (int db = 0; db < L::NDB; ++db)
+          va[kb][t][db] = as_bf16x8(ld16(vs + ((db * 32 + lq) * L::VSTR + kb * 32 + 16 * t + 8 * hf) * 2));
+#pragma unroll
+    for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
+    sched_reads_ahead<L::NKB * 2 * L::NDB>();
     v_store(L::v_off(ST ^ 1));
     wait_vmem_all();
     __syncthreads();
