@@ -101,6 +101,58 @@ def cpu_baseline(w, raw, seconds: float):
                       f"threads with one BLAS thread each; FLOPs counted as for the GPU"}
 
 
+HBM_PEAK_GBS = 8000.0                           # MI355X published HBM3E bandwidth
+
+
+def bench_decode(a, w):
+    """Split-key forward on a decoding workload (few query rows, long key cache).
+
+    Bound by the HBM read of K and V: the value is algorithmic bytes per step
+    (Q, K, V read once; O and lse written once) / time per step, against the HBM
+    peak.  One step = fa_fwd_splitkv (partials pass + merge pass)."""
+    import torch
+    import io_aware_exact_02_amd as fa
+    from io_aware_exact_02_amd.inputs import draw_workload
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] drawing inputs for {w.name}")
+    raw = draw_workload(w, with_do=False)
+    q, k, v = (torch.from_numpy(raw[n].view("int16")).view(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    B, H, Tq, Tk, d = w.B, w.H, w.Tq, w.Tk, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    nbytes = fa.fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    step = lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, ws, causal=w.causal, stream=stream)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    ms_ev = e0.elapsed_time(e1) / a.steps
+    alg_bytes = 2 * (2 * B * H * Tk * d + 2 * B * H * Tq * d) + 4 * B * H * Tq
+    gbs = alg_bytes / (ms_ev * 1e-3) / 1e9
+    out = {
+        "metric": f"split-key decode HBM GB/s ({w.name})", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": w.name, "B": B, "H": H, "Tq": Tq, "Tk": Tk, "d": d, "causal": w.causal,
+                   "pass": "forward (split-key)", "partials": nbytes // (4 * B * H * Tq * (d + 4))},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_partial_kernel+merge"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +174,8 @@ def main(argv=None):
     from io_aware_exact_02_amd.inputs import WORKLOADS, draw_workload
 
     w = WORKLOADS[a.workload]
+    if w.Tq <= 32 and w.dtype == "bf16" and not w.backward:
+        return bench_decode(a, w)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1

@@ -131,6 +131,30 @@ int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, co
                   int dtype, int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
                   int phases, void* stream);
 
+/*
+ * Split-key forward for few query rows per head (decoding) -- the same
+ * operation as fa_fwd, for bf16 inputs and d in {64, 128}.  With one or a few
+ * queries per head the query-block grid is too small to fill the GPU, so the
+ * keys of each head are also split into `nsplit` chunks; every chunk yields
+ * partial results (running maximum, weight sums, unnormalised O) that a second
+ * pass merges with the online-softmax rule ([Atlas] "Online softmax: the trick
+ * that makes tiling exact"; [ZtF] "The forward pass", steps 2.3-2.5).
+ *   nsplit     number of key chunks per 32-query block; 0 lets the library
+ *              choose (a fixed function of B, H, Tq, Tk)
+ *   workspace  device buffer of at least fa_fwd_splitkv_workspace_bytes(...)
+ *              bytes for the partials, owned by the caller, contents on entry
+ *              irrelevant
+ * Other arguments, layouts and outputs as fa_fwd.  Errors as fa_fwd, plus
+ * FA_ERR_DTYPE for float32 inputs, FA_ERR_HEADDIM for d = 256, FA_ERR_SHAPE for
+ * nsplit < 0 and FA_ERR_WORKSPACE for a missing or short workspace.  The
+ * partials are merged in a fixed order: results repeat bit for bit.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Tq, int Tk, int d, int nsplit);
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* lse,
+                   int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                   int dtype, int out_dtype, int nsplit, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Static, human-readable text for an fa_status value (never NULL). */
 const char* fa_strerror(int status);
 

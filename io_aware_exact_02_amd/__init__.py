@@ -22,14 +22,14 @@ import os
 __all__ = [
     "FA_F32", "FA_BF16", "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_POST", "FA_BWD_ALL", "FAError", "LIB_PATH", "library", "fa_fwd", "fa_bwd",
     "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
-    "EXPORTED_SYMBOLS",
+    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "forward_splitkv", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32 = 0
 FA_BF16 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror",
-                    "fa_abi_version")
+                    "fa_abi_version", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes")
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST, FA_BWD_ALL = 1, 2, 4, 7
 
 _lib = None
@@ -64,6 +64,10 @@ def library() -> ctypes.CDLL:
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
     lib.fa_abi_version.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -137,6 +141,32 @@ def fa_fwd(q, k, v, o, lse, *, scale=None, causal=False, stream=None) -> None:
         raise FAError(st, "fa_fwd")
 
 
+def fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, nsplit=0) -> int:
+    return int(library().fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, nsplit))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, workspace, *, scale=None, causal=False, nsplit=0, stream=None) -> None:
+    """Split-key forward (bf16 inputs, few query rows) into caller-provided `o`, `lse`;
+    `workspace` is a uint8 device tensor of fa_fwd_splitkv_workspace_bytes(...) bytes."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    _check(k, "k", (B, H, Tk, d), q.dtype, dev)
+    _check(v, "v", (B, H, Tk, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    _check(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = library().fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, H, Tq, Tk, d, c, int(bool(causal)), _dtype_code(q), _dtype_code(o),
+                                  int(nsplit), workspace.data_ptr(), workspace.numel(),
+                                  _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_fwd_splitkv")
+
+
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, *, scale=None, causal=False, stream=None) -> None:
     """Launch the backward pass into caller-provided dq, dk, dv (bf16 or fp32).
 
@@ -183,6 +213,21 @@ def forward(q, k, v, *, causal=False, scale=None, out_dtype=None, stream=None):
     o = torch.empty(q.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, stream=stream)
+    return o, lse
+
+
+def forward_splitkv(q, k, v, *, causal=False, scale=None, out_dtype=None, nsplit=0, stream=None):
+    """Allocate O, lse and the partials' workspace with torch and run fa_fwd_splitkv."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    o = torch.empty(q.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, nsplit)
+    if nbytes == 0:
+        raise ValueError("invalid arguments for fa_fwd_splitkv")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    fa_fwd_splitkv(q, k, v, o, lse, ws, scale=scale, causal=causal, nsplit=nsplit, stream=stream)
     return o, lse
 
 

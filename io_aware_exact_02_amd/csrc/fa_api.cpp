@@ -40,7 +40,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128, 256)";
     case FA_ERR_DTYPE: return "unsupported dtype or dtype combination";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than the *_workspace_bytes() size";
     case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
     case FA_ERR_PHASE: return "unknown bits in the backward phase mask";
@@ -101,6 +101,32 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return fa_bwd_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype,
                        grad_dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Tq, int Tk, int d, int nsplit) {
+  if (check_common(B, H, Tq, Tk, d, 1.f, FA_BF16) != FA_OK || d == 256 || nsplit < 0) return 0;
+  const long long parts = 4LL * fa::splitkv_parts(B, H, Tq, Tk, nsplit);
+  const long long rows = (long long)B * H * Tq;
+  return (size_t)(parts * rows * (d + 4) * (long long)sizeof(float));
+}
+
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
+                   int d, float scale, int causal, int dtype, int out_dtype, int nsplit, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, Tq, Tk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16 || !valid_dtype(out_dtype)) return FA_ERR_DTYPE;
+  if (d == 256) return FA_ERR_HEADDIM;
+  if (nsplit < 0) return FA_ERR_SHAPE;
+  const size_t need = fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, nsplit);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {Q, K, V, O, lse, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  return fa::launch_decode_bf16(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal ? 1 : 0,
+                                out_dtype == FA_F32 ? 1 : 0, fa::splitkv_parts(B, H, Tq, Tk, nsplit), workspace,
+                                static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -19,6 +19,12 @@ int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, 
 int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                    void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                    void* workspace, int phases, hipStream_t stream);
+// Split-key forward for few query rows: nsplit key chunks per 32-query block,
+// four partials per chunk (one per wave); splitkv_parts resolves nsplit = 0.
+int splitkv_parts(int B, int H, int Tq, int Tk, int nsplit);
+int launch_decode_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
+                       int Tk, int d, float scale, int causal, int out_f32, int nsplit, void* workspace,
+                       hipStream_t stream);
 int launch_rowdot_bf16(const void* dO, const void* O, int o_f32, float* Dout, long long rows, int d,
                        hipStream_t stream);
 

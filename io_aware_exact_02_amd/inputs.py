@@ -71,6 +71,9 @@ WORKLOADS = {
     "cross_bf16_b16h16_tq1024_tk8192_d128": Workload("cross_bf16_b16h16_tq1024_tk8192_d128", 16, 16, 1024, 8192,
                                                      128, "bf16", False, True, qk_spread=3.0,
                                                      seed=BASE_SEED + 5),
+    # decoding: one query row per head against a long key cache (split-key forward)
+    "decode_bf16_b8h16_tq1_tk32768_d128": Workload("decode_bf16_b8h16_tq1_tk32768_d128", 8, 16, 1, 32768, 128,
+                                                   "bf16", False, False, seed=BASE_SEED + 6),
 }
 
 

@@ -131,3 +131,37 @@ def test_bwd_phase_mask(lib):
     assert lib.fa_bwd_phases(*args, 0, None) == OK          # checks only, launches nothing
     bad = list(args); bad[0] = None
     assert lib.fa_bwd_phases(*bad, 0, None) == NULL
+
+
+def _dec(lib, ws=P, ws_bytes=1 << 30, B=1, H=1, Tq=1, Tk=100, d=128, scale=0.125, dtype=fa.FA_BF16,
+         odtype=fa.FA_BF16, nsplit=0, null_at=None):
+    ptrs = [P] * 5
+    if null_at is not None:
+        ptrs[null_at] = None
+    return lib.fa_fwd_splitkv(*ptrs, B, H, Tq, Tk, d, scale, 0, dtype, odtype, nsplit, ws, ws_bytes, None)
+
+
+def test_splitkv_workspace_and_errors(lib):
+    # four partials (one per wave) per key chunk, each d floats of O~ plus 4 statistics per row
+    B, H, Tq, Tk, d = 2, 3, 5, 1000, 128
+    ns = 3
+    assert fa.fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, ns) == 4 * ns * B * H * Tq * (d + 4) * 4
+    auto = fa.fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, 0)
+    assert auto > 0 and auto % (4 * B * H * Tq * (d + 4) * 4) == 0
+    # more chunks than 32-key tiles are clamped to the tile count
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 64, 64, 50) == 4 * 2 * 1 * (64 + 4) * 4
+    assert fa.fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, 256, 0) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(B, H, Tq, Tk, d, -1) == 0
+    for i in range(5):
+        assert _dec(lib, null_at=i) == NULL, i
+    assert _dec(lib, Tk=0) == SHAPE
+    assert _dec(lib, nsplit=-2) == SHAPE
+    assert _dec(lib, d=256) == HEADDIM
+    assert _dec(lib, d=96) == HEADDIM
+    assert _dec(lib, dtype=fa.FA_F32, odtype=fa.FA_F32) == DTYPE
+    assert _dec(lib, odtype=9) == DTYPE
+    assert _dec(lib, scale=0.0) == SCALE
+    assert _dec(lib, ws=None) == WORKSPACE
+    need = fa.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 100, 128, 0)
+    assert _dec(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _dec(lib, ws=P + 4, ws_bytes=need) == ALIGN
