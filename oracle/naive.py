@@ -51,8 +51,10 @@ import numpy as np
 
 __all__ = [
     "scores_head", "probs_head", "forward_head", "backward_head",
-    "forward", "backward", "default_scale",
+    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK",
 ]
+
+MASK_BLOCK = 128   # side of a block-mask block, in query rows and in keys
 
 
 def default_scale(d: int) -> float:
@@ -68,8 +70,20 @@ def _visible(Tk: int, rows: np.ndarray, causal: bool) -> np.ndarray | None:
     return np.arange(Tk)[None, :] <= rows[:, None]
 
 
-def scores_head(q, k, scale, causal, rows=None):
-    """Scaled, masked scores S[rows, :] = c q k^T with -inf where masked."""
+def block_allowed(Tq: int, Tk: int, block_mask_h, rows=None) -> np.ndarray:
+    """Boolean [len(rows), Tk] from a block mask [ceil(Tq/128)][ceil(Tk/128)] of one head.
+
+    [ZtF] "Dropout, block-sparsity, and other real-kernel details": a block mask
+    says which (query block, key block) tiles exist; attention restricted to it is
+    the dense definition with every score outside the kept blocks set to -inf."""
+    bm = np.asarray(block_mask_h) != 0
+    rows = np.arange(Tq) if rows is None else np.asarray(rows)
+    return bm[rows // MASK_BLOCK][:, np.arange(Tk) // MASK_BLOCK]
+
+
+def scores_head(q, k, scale, causal, rows=None, block_mask=None):
+    """Scaled, masked scores S[rows, :] = c q k^T with -inf where masked
+    (causal and/or a block mask of this head)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
@@ -77,40 +91,50 @@ def scores_head(q, k, scale, causal, rows=None):
     vis = _visible(k.shape[0], rows, causal)
     if vis is not None:
         S = np.where(vis, S, -np.inf)
+    if block_mask is not None:
+        S = np.where(block_allowed(q.shape[0], k.shape[0], block_mask, rows), S, -np.inf)
     return S
 
 
 def _softmax_rows(S):
-    """Row softmax with the row maximum subtracted; also returns lse = m + ln l."""
+    """Row softmax with the row maximum subtracted; also returns lse = m + ln l.
+
+    A row with no visible key (possible only under a block mask) has no softmax;
+    it is given zero weights and lse = -inf, so its output and gradients are 0."""
     m = S.max(axis=1)
-    E = np.exp(S - m[:, None])          # exp(-inf) = 0 for masked entries
+    empty = ~np.isfinite(m)
+    m0 = np.where(empty, 0.0, m)
+    E = np.exp(S - m0[:, None])         # exp(-inf) = 0 for masked entries
     l = E.sum(axis=1)
-    return E / l[:, None], m + np.log(l)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        P = np.where(empty[:, None], 0.0, E / np.where(empty, 1.0, l)[:, None])
+        lse = np.where(empty, -np.inf, m0 + np.log(np.where(empty, 1.0, l)))
+    return P, lse
 
 
-def probs_head(q, k, scale, causal, rows=None):
+def probs_head(q, k, scale, causal, rows=None, block_mask=None):
     """P[rows, :] = softmax(S) and lse[rows] for one head."""
-    return _softmax_rows(scores_head(q, k, scale, causal, rows))
+    return _softmax_rows(scores_head(q, k, scale, causal, rows, block_mask))
 
 
-def forward_head(q, k, v, scale, causal, rows=None):
+def forward_head(q, k, v, scale, causal, rows=None, block_mask=None):
     """O[rows] = softmax(c q k^T) v and lse[rows] for one head.
 
     q [Tq, d], k [Tk, d], v [Tk, dv].  Each output row depends only on its own
     query and all keys, so a subset `rows` is computed exactly by the same
     definition (used where the full T x T matrix would not fit in memory).
     """
-    P, lse = probs_head(q, k, scale, causal, rows)
+    P, lse = probs_head(q, k, scale, causal, rows, block_mask)
     return P @ np.asarray(v, dtype=np.float64), lse
 
 
-def backward_head(q, k, v, do, scale, causal):
+def backward_head(q, k, v, do, scale, causal, block_mask=None):
     """Gradients of sum(O * dO) for one head: returns dQ, dK, dV, O, lse, D."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    P, lse = probs_head(q, k, scale, causal)
+    P, lse = probs_head(q, k, scale, causal, block_mask=block_mask)
     O = P @ v
     dV = P.T @ do
     dP = do @ v.T
@@ -140,11 +164,20 @@ def _one_blas_thread():
         return contextlib.nullcontext()
 
 
-def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None):
+def _head_mask(block_mask, h):
+    """The block mask of head h from [Hm][nqb][nkb] (Hm = 1 is shared by all heads)."""
+    if block_mask is None:
+        return None
+    bm = np.asarray(block_mask)
+    return bm[0] if bm.shape[0] == 1 else bm[h]
+
+
+def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_mask=None):
     """Batched forward over [B, H, T, d] arrays.
 
     heads: optional list of (b, h) pairs to compute (others are left NaN);
-    rows: optional query-row subset applied to every selected head.
+    rows: optional query-row subset applied to every selected head;
+    block_mask: optional uint8 [Hm][ceil(Tq/128)][ceil(Tk/128)], Hm in {1, H}.
     Returns O [B, H, n_rows, d] and lse [B, H, n_rows] in float64.
     """
     B, H, Tq, _ = Q.shape
@@ -155,7 +188,8 @@ def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None):
 
     def run(bh):
         b, h = bh
-        O[b, h], L[b, h] = forward_head(Q[b, h], K[b, h], V[b, h], scale, causal, rows)
+        O[b, h], L[b, h] = forward_head(Q[b, h], K[b, h], V[b, h], scale, causal, rows,
+                                        _head_mask(block_mask, h))
 
     ex, nw = _pool(workers)
     with _one_blas_thread() if nw > 1 else _nullctx(), ex:
@@ -163,7 +197,7 @@ def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None):
     return O, L
 
 
-def backward(Q, K, V, dO, scale, causal, heads=None, workers=None):
+def backward(Q, K, V, dO, scale, causal, heads=None, workers=None, block_mask=None):
     """Batched backward over [B, H, T, d] arrays; returns dQ, dK, dV, O, lse."""
     B, H, Tq, d = Q.shape
     Tk = K.shape[2]
@@ -177,7 +211,7 @@ def backward(Q, K, V, dO, scale, causal, heads=None, workers=None):
     def run(bh):
         b, h = bh
         dQ[b, h], dK[b, h], dV[b, h], O[b, h], L[b, h], _ = backward_head(
-            Q[b, h], K[b, h], V[b, h], dO[b, h], scale, causal)
+            Q[b, h], K[b, h], V[b, h], dO[b, h], scale, causal, _head_mask(block_mask, h))
 
     ex, nw = _pool(workers)
     with _one_blas_thread() if nw > 1 else _nullctx(), ex:
