@@ -155,6 +155,36 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                    int dtype, int out_dtype, int nsplit, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * Block-sparse attention ([ZtF] "Dropout, block-sparsity, and other real-kernel
+ * details"): the same operation as fa_fwd / fa_bwd restricted to the (query
+ * block, key block) tiles a block mask keeps.  Every score outside a kept tile
+ * is -inf, exactly as if it were masked out of the dense definition; causal
+ * masking, when asked for, applies on top.  Tiles the mask drops are never
+ * read or computed, so work and HBM traffic scale with the mask's density.
+ *   block_mask  device buffer of uint8 [mask_heads][ceil(Tq/128)][ceil(Tk/128)],
+ *               row-major; entry (h, i, j) != 0 keeps query rows 128i..128i+127
+ *               against keys 128j..128j+127 for head h (for every batch entry).
+ *               Owned by the caller, read only.
+ *   mask_heads  1 (one mask shared by all heads) or H (one per head)
+ * A query row whose mask row keeps no key (or, causal, no key at or before it)
+ * gets O = 0 and lse = -inf, and its dQ is 0; keys no kept row sees get dK =
+ * dV = 0.  bfloat16 inputs only; the backward takes d in {64, 128}.  Other
+ * arguments, layouts, workspace and outputs as fa_fwd / fa_bwd.  Errors as
+ * those, plus FA_ERR_NULL for a missing mask, FA_ERR_SHAPE for mask_heads not
+ * in {1, H} or more than 32768 blocks along Tq or Tk, FA_ERR_DTYPE for float32
+ * inputs and FA_ERR_HEADDIM for a d = 256 backward.  Results repeat bit for bit.
+ */
+int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* lse,
+                  int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                  int dtype, int out_dtype, const unsigned char* block_mask, int mask_heads,
+                  void* stream);
+int fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* lse, void* dQ, void* dK, void* dV,
+                  int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                  int dtype, int o_dtype, int grad_dtype, const unsigned char* block_mask,
+                  int mask_heads, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for an fa_status value (never NULL). */
 const char* fa_strerror(int status);
 

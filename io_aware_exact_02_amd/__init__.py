@@ -22,14 +22,17 @@ import os
 __all__ = [
     "FA_F32", "FA_BF16", "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_POST", "FA_BWD_ALL", "FAError", "LIB_PATH", "library", "fa_fwd", "fa_bwd",
     "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
-    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "forward_splitkv", "EXPORTED_SYMBOLS",
+    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "forward_splitkv", "fa_fwd_masked", "fa_bwd_masked",
+    "forward_masked", "backward_masked", "MASK_BLOCK", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32 = 0
 FA_BF16 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror",
-                    "fa_abi_version", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes")
+                    "fa_abi_version", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_masked",
+                    "fa_bwd_masked")
+MASK_BLOCK = 128          # block-mask granularity, in query rows and in keys
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST, FA_BWD_ALL = 1, 2, 4, 7
 
 _lib = None
@@ -66,6 +69,10 @@ def library() -> ctypes.CDLL:
     lib.fa_abi_version.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp, sz, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_masked.argtypes = lib.fa_fwd.argtypes[:-1] + [vp, i, vp]
+    lib.fa_fwd_masked.restype = i
+    lib.fa_bwd_masked.argtypes = lib.fa_bwd.argtypes[:19] + [vp, i, vp, sz, vp]
+    lib.fa_bwd_masked.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     _lib = lib
@@ -204,6 +211,67 @@ def fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, workspace, phases, *, scale=N
         raise FAError(st, "fa_bwd_phases")
 
 
+def _check_mask(block_mask, H, Tq, Tk, dev):
+    torch = _torch()
+    nqb, nkb = -(-Tq // MASK_BLOCK), -(-Tk // MASK_BLOCK)
+    if block_mask.dim() != 3 or block_mask.shape[0] not in (1, H):
+        raise ValueError(f"block_mask: expected shape (1 or {H}, {nqb}, {nkb}), got {tuple(block_mask.shape)}")
+    _check(block_mask, "block_mask", (block_mask.shape[0], nqb, nkb), torch.uint8, dev)
+    return int(block_mask.shape[0])
+
+
+def fa_fwd_masked(q, k, v, o, lse, block_mask, *, scale=None, causal=False, stream=None) -> None:
+    """Block-sparse forward (bf16 inputs) into caller-provided `o`, `lse`.
+
+    `block_mask`: uint8 GPU tensor [1 or H, ceil(Tq/128), ceil(Tk/128)]; a non-zero
+    entry keeps that (128-query, 128-key) tile."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    _check(k, "k", (B, H, Tk, d), q.dtype, dev)
+    _check(v, "v", (B, H, Tk, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    mh = _check_mask(block_mask, H, Tq, Tk, dev)
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = library().fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 B, H, Tq, Tk, d, c, int(bool(causal)), _dtype_code(q), _dtype_code(o),
+                                 block_mask.data_ptr(), mh, _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_fwd_masked")
+
+
+def fa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace, *, scale=None, causal=False,
+                  stream=None) -> None:
+    """Block-sparse backward (bf16 inputs, d in {64, 128}) into caller-provided dq, dk, dv."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    for name, t, T in (("k", k, Tk), ("v", v, Tk), ("do", do, Tq)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    _check(dq, "dq", (B, H, Tq, d), None, dev)
+    _check(dk, "dk", (B, H, Tk, d), dq.dtype, dev)
+    _check(dv, "dv", (B, H, Tk, d), dq.dtype, dev)
+    mh = _check_mask(block_mask, H, Tq, Tk, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = library().fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk, d, c,
+                                 int(bool(causal)), _dtype_code(q), _dtype_code(o), _dtype_code(dq),
+                                 block_mask.data_ptr(), mh, workspace.data_ptr(), nbytes,
+                                 _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_bwd_masked")
+
+
 def forward(q, k, v, *, causal=False, scale=None, out_dtype=None, stream=None):
     """Allocate O and lse with torch and run fa_fwd.  Returns (O, lse).
 
@@ -249,4 +317,31 @@ def backward(q, k, v, o, do, lse, *, causal=False, scale=None, grad_dtype=None, 
         raise ValueError("invalid arguments for fa_bwd")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale=scale, causal=causal, stream=stream)
+    return dq, dk, dv
+
+
+def forward_masked(q, k, v, block_mask, *, causal=False, scale=None, out_dtype=None, stream=None):
+    """Allocate O and lse with torch and run fa_fwd_masked.  Returns (O, lse)."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    o = torch.empty(q.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    fa_fwd_masked(q, k, v, o, lse, block_mask, scale=scale, causal=causal, stream=stream)
+    return o, lse
+
+
+def backward_masked(q, k, v, o, do, lse, block_mask, *, causal=False, scale=None, grad_dtype=None, stream=None):
+    """Allocate gradients and workspace with torch and run fa_bwd_masked.  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty((B, H, Tq, d), dtype=gd, device=q.device)
+    dk = torch.empty((B, H, Tk, d), dtype=gd, device=q.device)
+    dv = torch.empty((B, H, Tk, d), dtype=gd, device=q.device)
+    nbytes = fa_bwd_workspace_bytes(B, H, Tq, Tk, d, _dtype_code(q), _dtype_code(dq))
+    if nbytes == 0:
+        raise ValueError("invalid arguments for fa_bwd_masked")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    fa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, block_mask, ws, scale=scale, causal=causal, stream=stream)
     return dq, dk, dv

@@ -26,6 +26,21 @@ int check_common(int B, int H, int Tq, int Tk, int d, float scale, int dtype) {
   return FA_OK;
 }
 
+// block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)] bytes; the kernels keep a
+// mask row or column as a bitmap of at most 32768 bits in LDS
+int check_mask(const unsigned char* block_mask, int mask_heads, int H, int Tq, int Tk, int dtype) {
+  if (!block_mask) return FA_ERR_NULL;
+  if (mask_heads != 1 && mask_heads != H) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if ((Tq + 127) / 128 > 32768 || (Tk + 127) / 128 > 32768) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
+             void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
+             int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads, void* workspace,
+             size_t workspace_bytes, int phases, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -76,9 +91,56 @@ int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, co
                   void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                   int dtype, int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes, int phases,
                   void* stream) {
+  return bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype, grad_dtype,
+                  nullptr, 1, workspace, workspace_bytes, phases, stream);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
+           void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
+           int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype,
+                       grad_dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
+int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
+                  int d, float scale, int causal, int dtype, int out_dtype, const unsigned char* block_mask,
+                  int mask_heads, void* stream) {
+  if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, Tq, Tk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_mask(block_mask, mask_heads, H, Tq, Tk, dtype);
+  if (st != FA_OK) return st;
+  if (!valid_dtype(out_dtype)) return FA_ERR_DTYPE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse)) return FA_ERR_ALIGN;
+  return fa::launch_fwd_bf16(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal ? 1 : 0, out_dtype == FA_F32 ? 1 : 0,
+                             static_cast<hipStream_t>(stream), block_mask, mask_heads);
+}
+
+int fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                  void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                  int dtype, int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!block_mask) return FA_ERR_NULL;
+  return bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype, grad_dtype,
+                  block_mask, mask_heads, workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
+             void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
+             int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads, void* workspace,
+             size_t workspace_bytes, int phases, void* stream) {
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return FA_ERR_NULL;
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
+  if (block_mask) {
+    st = check_mask(block_mask, mask_heads, H, Tq, Tk, dtype);
+    if (st != FA_OK) return st;
+    if (d == 256) return FA_ERR_HEADDIM;
+  }
   if (!valid_dtype(grad_dtype) || (dtype == FA_F32 && grad_dtype != FA_F32)) return FA_ERR_DTYPE;
   if (!valid_dtype(o_dtype) || (dtype == FA_F32 && o_dtype != FA_F32)) return FA_ERR_DTYPE;
   if (phases & ~FA_BWD_ALL) return FA_ERR_PHASE;
@@ -92,16 +154,14 @@ int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, co
   causal = causal ? 1 : 0;
   if (dtype == FA_BF16)
     return fa::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal,
-                               o_dtype == FA_F32 ? 1 : 0, grad_dtype == FA_F32 ? 1 : 0, workspace, phases, s);
+                               o_dtype == FA_F32 ? 1 : 0, grad_dtype == FA_F32 ? 1 : 0, workspace, phases, s,
+                               block_mask, mask_heads);
   return fa::launch_bwd_f32(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, workspace, phases, s);
 }
 
-int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
-           void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
-           int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return fa_bwd_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype,
-                       grad_dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
-}
+}  // namespace
+
+extern "C" {
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Tq, int Tk, int d, int nsplit) {
   if (check_common(B, H, Tq, Tk, d, 1.f, FA_BF16) != FA_OK || d == 256 || nsplit < 0) return 0;

@@ -444,13 +444,26 @@ struct KvLayout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL>
+// Block-sparse sweeps ([ZtF] "Dropout, block-sparsity, and other real-kernel
+// details"): the mask holds one byte per (128-query block, 128-key block); a
+// key block's workgroup first gathers its mask column into an LDS bitmap (bit r
+// = query block r may attend to it) and then visits only the query tiles whose
+// block bit is set.  Each role walks the same tile sequence with its own cursor,
+// so both still pass the same number of barriers.
+constexpr int kMaskBlock = 128;
+constexpr int kVisWords = 512;                  // bitmap words: up to 32768 query blocks
+constexpr int kTilesPerMaskRow = kMaskBlock / kBQ;
+static_assert(kBKC == kMaskBlock, "one key-block workgroup per mask column");
+
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
-    void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e, int nkb, int grad_f32) {
+    void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e, int nkb, int grad_f32,
+    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk) {
   using L = KvLayout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  __shared__ unsigned long long vis[MASKED ? kVisWords : 1];
 
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
@@ -467,8 +480,60 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 
   const int nqt = (Tq + kBQ - 1) / kBQ;
   const int it0 = CAUSAL ? min(k0 / kBQ, nqt) : 0;
-  const int n = nqt - it0;                      // query tiles in the sweep
-  auto first_row = [&](int s) { return it0 + s < nqt ? (it0 + s) * kBQ : Tq; };
+  // tile t covers query rows t kBQ ..; a tile past the sweep reads row Tq (zeros)
+  auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
+
+  // visible query tiles: all from it0 on, or (masked) those whose block bit is set
+  const int nmq = (Tq + kMaskBlock - 1) / kMaskBlock;
+  const int nvw = (nmq + 63) >> 6;
+  auto vis_word = [&](int w) {
+    const unsigned long long x = vis[w];
+    return ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32)) << 32) |
+           __builtin_amdgcn_readfirstlane((unsigned)x);
+  };
+  auto vis_row = [&](int r) { return ((vis_word(r >> 6) >> (r & 63)) & 1ull) != 0; };
+  auto next_row = [&](int r) {                  // first visible query block >= r, nmq if none
+    int w = r >> 6;
+    if (w >= nvw) return nmq;
+    unsigned long long bits = vis_word(w) & (~0ull << (r & 63));
+    while (bits == 0) {
+      if (++w >= nvw) return nmq;
+      bits = vis_word(w);
+    }
+    return w * 64 + (int)__builtin_ctzll(bits);
+  };
+  auto next_tile = [&](int t) {                 // first visible tile >= t (nqt if none)
+    if constexpr (MASKED) {
+      if (t >= nqt) return nqt;
+      if (vis_row(t / kTilesPerMaskRow)) return t;
+      const int r = next_row(t / kTilesPerMaskRow + 1);
+      return r < nmq ? r * kTilesPerMaskRow : nqt;
+    } else {
+      return t;
+    }
+  };
+  int n = nqt - it0;                            // query tiles in the sweep
+  if constexpr (MASKED) {
+    const uint8_t* mcol = bmask + (long long)(bh % H) * mask_hstride + kblk;
+    for (int w = wave; w < nvw; w += 8) {
+      const int r = w * 64 + lane;
+      const unsigned long long bits = __ballot(r < nmq && mcol[(long long)r * nmk] != 0);
+      if (lane == 0) vis[w] = bits;
+    }
+    __syncthreads();
+    n = 0;
+    if (it0 < nqt) {
+      const int rlo = it0 / kTilesPerMaskRow;
+      for (int w = rlo >> 6; w < nvw; ++w) {
+        unsigned long long bits = vis_word(w);
+        if (w == (rlo >> 6)) bits &= ~0ull << (rlo & 63);
+        n += __builtin_popcountll(bits);
+      }
+      n *= kTilesPerMaskRow;
+      if (vis_row(rlo)) n -= it0 - rlo * kTilesPerMaskRow;          // first block starts at it0
+      if (vis_row(nmq - 1)) n -= nmq * kTilesPerMaskRow - nqt;      // last block is ragged
+    }
+  }
 
   if (wave < 4) {
     // ============================ score waves ============================
@@ -485,8 +550,8 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     }
     // -lse log2e and -D of the tile's queries in the accumulator order:
     // register r <-> query 8(r/4) + 4hf + r%4 (all lanes of a half alike)
-    auto terms_load = [&](int s, f32x16& lt, f32x16& dt) {
-      const int r0 = first_row(s);
+    auto terms_load = [&](int t, f32x16& lt, f32x16& dt) {
+      const int r0 = tile_row(t);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const unsigned off = (unsigned)(r0 + 8 * g4 + 4 * hf) * 4u;
@@ -500,13 +565,16 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       }
     };
     f32x16 lt0, dt0, lt1, dt1;
-    terms_load(0, lt0, dt0);
+    int tc = next_tile(it0);                      // the tile of the next score step
+    terms_load(tc, lt0, dt0);
     __syncthreads();
 
-    auto score_step = [&](int s, auto stage, const f32x16& lt, const f32x16& dt, f32x16& lt_n, f32x16& dt_n) {
-      constexpr int ST = decltype(stage)::value;      // s % 2
-      terms_load(s + 1, lt_n, dt_n);
-      const int r0 = (it0 + s) * kBQ;
+    // tile t in stage ST (the step's parity in the sweep); tn is the tile after it
+    auto score_step = [&](int t, int tn, auto stage, const f32x16& lt, const f32x16& dt, f32x16& lt_n,
+                          f32x16& dt_n) {
+      constexpr int ST = decltype(stage)::value;
+      terms_load(tn, lt_n, dt_n);
+      const int r0 = t * kBQ;
       const char* sb_ = smem + ST * L::STAGE;
       // S = Q_i K_j^T and dP - D = dO_i V_j^T - D_i: lane = key, register r = query 8(r/4)+4hf+r%4
       f32x16 sacc, dp = dt;
@@ -549,8 +617,14 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       __syncthreads();
     };
     for (int s = 0; s < n; s += 2) {
-      score_step(s, std::integral_constant<int, 0>{}, lt0, dt0, lt1, dt1);
-      if (s + 1 < n) score_step(s + 1, std::integral_constant<int, 1>{}, lt1, dt1, lt0, dt0);
+      int tn = next_tile(tc + 1);
+      score_step(tc, tn, std::integral_constant<int, 0>{}, lt0, dt0, lt1, dt1);
+      tc = tn;
+      if (s + 1 < n) {
+        tn = next_tile(tc + 1);
+        score_step(tc, tn, std::integral_constant<int, 1>{}, lt1, dt1, lt0, dt0);
+        tc = tn;
+      }
     }
   } else {
     // =========================== gradient waves ==========================
@@ -571,9 +645,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const int n_off = (is_g ? L::G_N : L::Q_N) + ((4 * qa) * L::NSTR + fg * 8) * 2;
     const int t_off = (is_g ? L::GT_OFF : L::QT_OFF) + ((fg * 8) * L::TSTR + tpos) * 2;
     u32x4 stg[4];
-    auto gload = [&](int s) {
+    auto gload = [&](int t) {
       if (stager) {
-        const int r0 = first_row(s);
+        const int r0 = tile_row(t);
 #pragma unroll
         for (int i = 0; i < 4; ++i) stg[i] = bload16(rsrc, ((unsigned)(r0 + 4 * qa + i) * D + fg * 8) * 2u);
       }
@@ -633,21 +707,29 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       sched_reads_ahead<4 * L::NDB, 4 * L::NDB + 4>();
     };
 
+    int tg = next_tile(it0);                         // the tile of the next fetch
     if (n > 0) {
-      gload(0);
+      gload(tg);
       lstore(0, 0);
-      if (n > 1) gload(1);
+      tg = next_tile(tg + 1);
+      if (n > 1) {
+        gload(tg);
+        tg = next_tile(tg + 1);
+      }
     }
     __syncthreads();
-    // phase p: gradients of tile p-1, stage tile p+1, fetch tile p+2.  m2 = p % 2
-    // and m3 = p % 3 (wave-uniform counters) pick the slots.
+    // phase p: gradients of sweep step p-1, stage step p+1, fetch step p+2.
+    // m2 = p % 2 and m3 = p % 3 (wave-uniform counters) pick the slots.
     int m2 = 0, m3 = 0;
     for (int p = 0; p < n; ++p) {
       const int up3 = m3 == 2 ? 0 : m3 + 1;          // (p + 1) % 3
       const int dn3 = m3 == 0 ? 2 : m3 - 1;          // (p - 1) % 3
       if (p >= 1) grad_step(m2 ^ 1, dn3);
       if (p + 1 < n) lstore(m2 ^ 1, up3);
-      if (p + 2 < n) gload(p + 2);
+      if (p + 2 < n) {
+        gload(tg);
+        tg = next_tile(tg + 1);
+      }
       __syncthreads();
       m2 ^= 1;
       m3 = up3;
@@ -731,14 +813,21 @@ struct DqLayout {
 template <int NC>
 __device__ __forceinline__ int dq_swz(int r) { return NC >= 16 ? (r & 15) : ((r >> 1) & 7); }
 
-template <int D, bool CAUSAL>
+// Block-sparse dQ sweep: the workgroup's 256 queries span two 128-query mask
+// rows.  Both rows go into LDS bitmaps (bit c = key block c visible); the
+// workgroup visits the key tiles that either row can see, and a wave computes
+// only those its own row can see.
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
-    void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32) {
+    void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32,
+    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk) {
   using L = DqLayout<D>;
   constexpr int BC = L::BC;
+  static_assert(kMaskBlock % BC == 0 && kDqBR == 2 * kMaskBlock, "two mask rows, whole tiles per mask block");
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+  __shared__ unsigned long long vis[MASKED ? 2 * kVisWords : 1];
 
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
@@ -825,19 +914,65 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
 
+  // ---- visible key tiles
+  const int nvw = (nmk + 63) >> 6;
+  auto vis_word = [&](int w) {
+    const unsigned long long x = vis[w];
+    return ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32)) << 32) |
+           __builtin_amdgcn_readfirstlane((unsigned)x);
+  };
+  if constexpr (MASKED) {
+    const int mr = q0 / kMaskBlock;
+    const bool has_b = mr + 1 < (Tq + kMaskBlock - 1) / kMaskBlock;
+    const uint8_t* m = bmask + (long long)(bh % H) * mask_hstride + (long long)mr * nmk;
+    for (int i = wave; i < 2 * nvw; i += kDqWaves) {
+      const int row = i / nvw, w = i - row * nvw;
+      const int c = w * 64 + lane;
+      const unsigned long long bits = __ballot(c < nmk && (row == 0 || has_b) && m[(long long)row * nmk + c] != 0);
+      if (lane == 0) vis[row * kVisWords + w] = bits;
+    }
+    __syncthreads();
+  }
+  auto next_tile = [&](int j) {                       // first tile >= j either mask row sees, ntile if none
+    if constexpr (MASKED) {
+      if (j >= ntile) return ntile;
+      const int c = j * BC / kMaskBlock;
+      int w = c >> 6;
+      unsigned long long bits = (vis_word(w) | vis_word(kVisWords + w)) & (~0ull << (c & 63));
+      while (bits == 0) {
+        if (++w >= nvw) return ntile;
+        bits = vis_word(w) | vis_word(kVisWords + w);
+      }
+      const int c2 = w * 64 + (int)__builtin_ctzll(bits);
+      return c2 == c ? j : min(ntile, c2 * (kMaskBlock / BC));
+    } else {
+      return j;
+    }
+  };
+  auto wave_sees = [&](int j) {                       // this wave's mask row sees tile j
+    if constexpr (MASKED) {
+      const int c = j * BC / kMaskBlock;
+      return ((vis_word((wave >> 2) * kVisWords + (c >> 6)) >> (c & 63)) & 1ull) != 0;
+    } else {
+      return true;
+    }
+  };
+
   auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
-  kv_dma(0, 0);
-  t_load(0);
+  const int j0 = next_tile(0);
+  kv_dma(first_row(j0), 0);
+  t_load(first_row(j0));
   t_store(0);
   wait_vmem_all();
   __syncthreads();
 
-  auto step = [&](int j, auto stage) {
-    constexpr int ST = decltype(stage)::value;        // j % 2
-    t_load(first_row(j + 1));
-    kv_dma(first_row(j + 1), ST ^ 1);
+  // tile j in stage ST (the step's parity in the sweep); jn is the tile after it
+  auto step = [&](int j, int jn, auto stage) {
+    constexpr int ST = decltype(stage)::value;
+    t_load(first_row(jn));
+    kv_dma(first_row(jn), ST ^ 1);
     const int kt0 = j * BC;
-    if (!CAUSAL || kt0 <= qw + 31) {                  // some key of the block is visible to this wave
+    if ((!CAUSAL || kt0 <= qw + 31) && wave_sees(j)) {   // some key of the block is visible to this wave
       const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk);
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb) {
@@ -899,9 +1034,21 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     __syncthreads();
   };
 
-  for (int j = 0; j < ntile; j += 2) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < ntile) step(j + 1, std::integral_constant<int, 1>{});
+  if constexpr (MASKED) {
+    for (int j = j0; j < ntile;) {
+      int jn = next_tile(j + 1);
+      step(j, jn, std::integral_constant<int, 0>{});
+      j = jn;
+      if (j >= ntile) break;
+      jn = next_tile(j + 1);
+      step(j, jn, std::integral_constant<int, 1>{});
+      j = jn;
+    }
+  } else {
+    for (int j = 0; j < ntile; j += 2) {
+      step(j, j + 1, std::integral_constant<int, 0>{});
+      if (j + 1 < ntile) step(j + 1, j + 2, std::integral_constant<int, 1>{});
+    }
   }
 
   if (myq >= Tq) return;
@@ -947,7 +1094,7 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
 template <int D>
 int bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
         void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int o_f32, int grad_f32,
-        void* workspace, int phases, hipStream_t stream) {
+        void* workspace, int phases, hipStream_t stream, const uint8_t* bmask, int mask_heads) {
   const long long rows = (long long)B * H * Tq;
   const long long nq = rows * D;
   const int nkb = (Tk + kBKC - 1) / kBKC;
@@ -962,7 +1109,12 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
   auto v = static_cast<const uint16_t*>(V);
   auto g = static_cast<const uint16_t*>(dO);
   float* Dws = static_cast<float*>(workspace);
+  // block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)]
+  const int nmq = (Tq + kMaskBlock - 1) / kMaskBlock, nmk = (Tk + kMaskBlock - 1) / kMaskBlock;
+  const long long mhs = mask_heads == 1 ? 0 : (long long)nmq * nmk;
+  if (bmask && (nmq > 64 * kVisWords || nmk > 64 * kVisWords)) return FA_ERR_SHAPE;
   if constexpr (D == 256) {
+    if (bmask) return FA_ERR_HEADDIM;
     // one key-block sweep that also adds dQ contributions into a float32 accumulator
     float* acc = grad_f32 ? static_cast<float*>(dQ) : Dws + bwd_rows_padded(rows);
     if (phases & FA_BWD_PRE) {
@@ -998,20 +1150,30 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
                            rows);
     }
     if (phases & FA_BWD_MAIN) {
-      if (causal)
-        hipLaunchKernelGGL((bwd_kv_kernel<D, true>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, Ln, Dn,
-                           dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
-      else
-        hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, Ln,
-                           Dn, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
+      auto kv = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, Ln, Dn, dK, dV, Tq, Tk,
+                           scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk);
+      };
+      if (bmask) {
+        if (causal) kv(bwd_kv_kernel<D, true, true>);
+        else kv(bwd_kv_kernel<D, false, true>);
+      } else {
+        if (causal) kv(bwd_kv_kernel<D, true, false>);
+        else kv(bwd_kv_kernel<D, false, false>);
+      }
     }
     if (phases & FA_BWD_POST) {
-      if (causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, Ln,
-                           Dn, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
-      else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, Ln,
-                           Dn, dQ, Tq, Tk, scale, cl2e, nqb, grad_f32);
+      auto dqk = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq, Tk,
+                           scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk);
+      };
+      if (bmask) {
+        if (causal) dqk(bwd_dq_kernel<D, true, true>);
+        else dqk(bwd_dq_kernel<D, false, true>);
+      } else {
+        if (causal) dqk(bwd_dq_kernel<D, true, false>);
+        else dqk(bwd_dq_kernel<D, false, false>);
+      }
     }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -1021,11 +1183,12 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
 
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                    int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream) {
+                    int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream, const uint8_t* bmask,
+                    int mask_heads) {
   switch (d) {
-    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream);
-    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream);
-    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream);
+    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads);
+    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads);
+    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads);
     default: return FA_ERR_HEADDIM;
   }
 }

@@ -81,11 +81,12 @@ struct FwdLayout {
 template <int NC>
 __device__ __forceinline__ int kswz(int r) { return NC >= 16 ? (r & 15) : ((r >> 1) & 7); }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_EU)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, void* __restrict__ O,
-                     float* __restrict__ lse, int Tq, int Tk, float cl2e, int nqb) {
+                     float* __restrict__ lse, int Tq, int Tk, float cl2e, int nqb,
+                     const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk) {
   using L = FwdLayout<D>;
   constexpr int BC = L::BC;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
@@ -207,21 +208,39 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   };
 
-  // ---- prologue: K_0 and V_0 into LDS stage 0
+  // Key blocks the sweep visits: all of them, or (block mask, [ZtF] "Dropout,
+  // block-sparsity, and other real-kernel details") only those whose 128-key
+  // mask block is kept for this 128-row block; next_tile(j) is the first
+  // visited block at or after j (ntile when none is left).
+  static_assert(kBR == 128 && 128 % BC == 0, "one mask row per query block, whole key blocks per mask block");
+  const uint8_t* mrow = MASKED ? bmask + (bh % H) * mask_hstride + (long long)qb * nmk : nullptr;
+  auto next_tile = [&](int j) {
+    if constexpr (MASKED) {
+      // the byte is the same for every lane: readfirstlane keeps the loop wave-uniform
+      while (j < ntile && __builtin_amdgcn_readfirstlane(mrow[(j * BC) >> 7]) == 0)
+        j = ((((j * BC) >> 7) + 1) << 7) / BC;
+      return j < ntile ? j : ntile;
+    } else {
+      return j;
+    }
+  };
+
+  // ---- prologue: the first visited K and V block into LDS stage 0
   // A block index past the sweep maps to row Tk: its loads return zeros and
   // move no data, so the steps below need no branches around their loads.
   auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
-  k_dma(0, L::k_off(0));
-  v_load(0);
+  const int j0 = next_tile(0);
+  k_dma(first_row(j0), L::k_off(0));
+  v_load(first_row(j0));
   v_store(L::v_off(0));
   wait_vmem_all();
   __syncthreads();
 
-  auto step = [&](int j, auto stage) {
-    constexpr int ST = decltype(stage)::value;        // j % 2
-    // block j+1 in flight: K straight into LDS, V into registers
-    v_load(first_row(j + 1));
-    k_dma(first_row(j + 1), L::k_off(ST ^ 1));
+  auto step = [&](int j, int jn, auto stage) {
+    constexpr int ST = decltype(stage)::value;        // position of block j in the sweep, mod 2
+    // the next visited block jn in flight: K straight into LDS, V into registers
+    v_load(first_row(jn));
+    k_dma(first_row(jn), L::k_off(ST ^ 1));
     f32x16 s[L::NKB];
     s_product(s, L::k_off(ST));
     mask_tile(s, j);
@@ -292,16 +311,29 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     __syncthreads();
   };
 
-  for (int j = 0; j < ntile; j += 2) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < ntile) step(j + 1, std::integral_constant<int, 1>{});
+  if constexpr (MASKED) {
+    for (int j = j0; j < ntile;) {
+      int jn = next_tile(j + 1);
+      step(j, jn, std::integral_constant<int, 0>{});
+      j = jn;
+      if (j >= ntile) break;
+      jn = next_tile(j + 1);
+      step(j, jn, std::integral_constant<int, 1>{});
+      j = jn;
+    }
+  } else {
+    for (int j = 0; j < ntile; j += 2) {
+      step(j, j + 1, std::integral_constant<int, 0>{});
+      if (j + 1 < ntile) step(j + 1, j + 2, std::integral_constant<int, 1>{});
+    }
   }
 
   if (qw >= Tq) return;
   const float l_tot = half_swap_sum(l_part);
   const float lr_tot = half_swap_sum(lr_part);
   if (myq >= Tq) return;
-  const float inv = 1.f / lr_tot;
+  // a row that sees no key (possible only under a block mask) gets O = 0, lse = -inf
+  const float inv = (!MASKED || lr_tot > 0.f) ? 1.f / lr_tot : 0.f;
 #pragma unroll
   for (int db = 0; db < L::NDB; ++db)
 #pragma unroll
@@ -318,19 +350,34 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         st8(static_cast<uint16_t*>(O) + off, w);
       }
     }
-  if (hf == 0) lse[(size_t)bh * Tq + myq] = (m_ref + log2f(l_tot)) * kLn2;
+  if (hf == 0)
+    lse[(size_t)bh * Tq + myq] = (!MASKED || l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool MASKED>
 void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
-                float* lse, int Tq, int Tk, float cl2e, int nqb) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32>), grid, dim3(256), 0, stream, q, k, v, o, lse, Tq, Tk,
-                     cl2e, nqb);
+                float* lse, int Tq, int Tk, float cl2e, int nqb, const uint8_t* bmask, int H, long long hstride,
+                int nmk) {
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, MASKED>), grid, dim3(256), 0, stream, q, k, v, o, lse, Tq,
+                     Tk, cl2e, nqb, bmask, H, hstride, nmk);
+}
+
+template <int D, bool MASKED>
+void launch_dtype(dim3 grid, hipStream_t stream, int causal, int out_f32, const uint16_t* q, const uint16_t* k,
+                  const uint16_t* v, void* O, float* lse, int Tq, int Tk, float cl2e, int nqb, const uint8_t* bmask,
+                  int H, long long hstride, int nmk) {
+  if (causal) {
+    if (out_f32) launch_one<D, true, true, MASKED>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+    else launch_one<D, true, false, MASKED>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+  } else {
+    if (out_f32) launch_one<D, false, true, MASKED>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+    else launch_one<D, false, false, MASKED>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+  }
 }
 
 template <int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
-           float scale, int causal, int out_f32, hipStream_t stream) {
+           float scale, int causal, int out_f32, const uint8_t* bmask, int mask_heads, hipStream_t stream) {
   const int nqb = (Tq + kBR - 1) / kBR;
   const long long nblk = (long long)nqb * B * H;
   if (nblk > 0x7fffffffLL) return FA_ERR_SHAPE;
@@ -339,24 +386,25 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int
   auto q = static_cast<const uint16_t*>(Q);
   auto k = static_cast<const uint16_t*>(K);
   auto v = static_cast<const uint16_t*>(V);
-  if (causal) {
-    if (out_f32) launch_one<D, true, true>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
-    else launch_one<D, true, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
-  } else {
-    if (out_f32) launch_one<D, false, true>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
-    else launch_one<D, false, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
-  }
+  // block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)]; the 128-row blocks are this kernel's query blocks
+  const int nmk = (Tk + 127) / 128;
+  const long long hstride = mask_heads == 1 ? 0 : (long long)nqb * nmk;
+  if (bmask)
+    launch_dtype<D, true>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+  else
+    launch_dtype<D, false>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace
 
 int launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H,
-                    int Tq, int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream) {
+                    int Tq, int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream,
+                    const uint8_t* bmask, int mask_heads) {
   switch (d) {
-    case 64: return launch<64>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, stream);
-    case 128: return launch<128>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, stream);
-    case 256: return launch<256>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, stream);
+    case 64: return launch<64>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, stream);
+    case 128: return launch<128>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, stream);
+    case 256: return launch<256>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, stream);
     default: return FA_ERR_HEADDIM;
   }
 }

@@ -9,13 +9,16 @@ namespace fa {
 // 64 floats (256 bytes), then (bf16 gradients only) the float32 dQ accumulator.
 inline long long bwd_rows_padded(long long rows) { return (rows + 63) / 64 * 64; }
 
+// bmask: optional block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)] (uint8, device memory)
 int launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
-                    int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream);
+                    int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream,
+                    const uint8_t* bmask = nullptr, int mask_heads = 1);
 int launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
                    int Tk, int d, float scale, int causal, hipStream_t stream);
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
-                    int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream);
+                    int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream,
+                    const uint8_t* bmask = nullptr, int mask_heads = 1);
 int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                    void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                    void* workspace, int phases, hipStream_t stream);

@@ -9,6 +9,12 @@ order Q, K, V, dO, each over its whole [B, H, T, d] shape; Q and K optionally
 multiplied by a spread (3 for the large-logit cross-attention workload); bf16
 tensors are the float32 draws rounded to nearest-even, and the oracle widens
 exactly those bf16 values to float64.
+
+Block masks (block-sparse attention): uint8 [heads][ceil(Tq/128)][ceil(Tk/128)]
+drawn as Bernoulli(density) per block from `default_rng(seed)` in row-major
+order (uniform draws < density), after which the listed forced blocks are set:
+the diagonal (i, i) when `keep_diagonal`, so that every query block sees at
+least one key block, and the rows in `empty_rows` cleared.
 """
 from __future__ import annotations
 
@@ -48,6 +54,7 @@ class Workload:
     backward: bool      # the workload includes the backward pass
     qk_spread: float = 1.0
     seed: int = BASE_SEED
+    mask_density: float | None = None   # block-sparse: fraction of kept 128 x 128 blocks (one mask per head)
 
     def flops_fwd(self) -> float:
         """4 B H Tq Tk d, halved when causal (square causal: visible pairs ~ T^2 / 2)."""
@@ -71,6 +78,10 @@ WORKLOADS = {
     "cross_bf16_b16h16_tq1024_tk8192_d128": Workload("cross_bf16_b16h16_tq1024_tk8192_d128", 16, 16, 1024, 8192,
                                                      128, "bf16", False, True, qk_spread=3.0,
                                                      seed=BASE_SEED + 5),
+    # block-sparse: a quarter of the 128 x 128 blocks of each head kept, diagonal always kept
+    "blocksparse_bf16_b8h32_t4096_d128_s25": Workload("blocksparse_bf16_b8h32_t4096_d128_s25", 8, 32, 4096, 4096,
+                                                      128, "bf16", False, True, seed=BASE_SEED + 7,
+                                                      mask_density=0.25),
     # decoding: one query row per head against a long key cache (split-key forward)
     "decode_bf16_b8h16_tq1_tk32768_d128": Workload("decode_bf16_b8h16_tq1_tk32768_d128", 8, 16, 1, 32768, 128,
                                                    "bf16", False, False, seed=BASE_SEED + 6),
@@ -104,3 +115,21 @@ def draw_workload(w: Workload, with_do=None):
 def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     """The exact float64 values of a drawn array (bf16 bits or float32)."""
     return bf16_bits_to_f32(a).astype(np.float64) if dtype == "bf16" else np.asarray(a, np.float64)
+
+
+def block_mask(heads, Tq, Tk, density, seed, keep_diagonal=True, empty_rows=()):
+    """A seeded block mask uint8 [heads][ceil(Tq/128)][ceil(Tk/128)] (recipe above)."""
+    nq, nk = -(-Tq // 128), -(-Tk // 128)
+    rng = np.random.default_rng(seed)
+    m = (rng.random((heads, nq, nk)) < density).astype(np.uint8)
+    if keep_diagonal:
+        i = np.arange(min(nq, nk))
+        m[:, i, i] = 1
+    for r in empty_rows:
+        m[:, r, :] = 0
+    return m
+
+
+def workload_mask(w: Workload):
+    """The block mask of a block-sparse workload: one per head, seeded from the workload."""
+    return block_mask(w.H, w.Tq, w.Tk, w.mask_density, w.seed + 1000)

@@ -165,3 +165,41 @@ def test_splitkv_workspace_and_errors(lib):
     need = fa.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 100, 128, 0)
     assert _dec(lib, ws_bytes=need - 1) == WORKSPACE
     assert _dec(lib, ws=P + 4, ws_bytes=need) == ALIGN
+
+
+def _mfwd(lib, mask=P, mheads=1, B=1, H=2, Tq=300, Tk=300, d=128, dtype=fa.FA_BF16, odtype=fa.FA_BF16,
+          null_at=None):
+    ptrs = [P] * 5
+    if null_at is not None:
+        ptrs[null_at] = None
+    return lib.fa_fwd_masked(*ptrs, B, H, Tq, Tk, d, 0.125, 0, dtype, odtype, mask, mheads, None)
+
+
+def _mbwd(lib, mask=P, mheads=1, B=1, H=2, Tq=300, Tk=300, d=128, dtype=fa.FA_BF16, ws=P, ws_bytes=1 << 30):
+    return lib.fa_bwd_masked(*([P] * 9), B, H, Tq, Tk, d, 0.125, 0, dtype, dtype, dtype, mask, mheads, ws,
+                             ws_bytes, None)
+
+
+def test_masked_argument_errors(lib):
+    """The block-sparse entry points: mask presence, its head count, dtype, head
+    dimension and block counts are checked before anything is launched."""
+    for i in range(5):
+        assert _mfwd(lib, null_at=i) == NULL, i
+    assert _mfwd(lib, mask=None) == NULL
+    assert _mbwd(lib, mask=None) == NULL
+    for mh in (0, 3, -1):
+        assert _mfwd(lib, mheads=mh) == SHAPE, mh
+        assert _mbwd(lib, mheads=mh) == SHAPE, mh
+    assert _mfwd(lib, dtype=fa.FA_F32, odtype=fa.FA_F32) == DTYPE
+    assert _mbwd(lib, dtype=fa.FA_F32) == DTYPE
+    assert _mfwd(lib, odtype=7) == DTYPE
+    assert _mbwd(lib, d=256) == HEADDIM           # the forward takes d = 256, the backward does not
+    assert _mfwd(lib, d=96) == HEADDIM
+    assert _mfwd(lib, Tq=0) == SHAPE
+    # more than 32768 mask blocks along a sequence (d = 64 keeps the size check of a slice happy)
+    assert _mfwd(lib, Tk=32768 * 128 + 1, d=64) == SHAPE
+    assert _mbwd(lib, Tq=32768 * 128 + 1, d=64) == SHAPE
+    assert _mbwd(lib, ws=None) == WORKSPACE
+    need = fa.fa_bwd_workspace_bytes(1, 2, 300, 300, 128, fa.FA_BF16, fa.FA_BF16)
+    assert _mbwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _mbwd(lib, ws=P + 8, ws_bytes=need) == ALIGN

@@ -1,0 +1,188 @@
+"""Block-sparse attention ([ZtF] "Dropout, block-sparsity, and other real-kernel
+details") through the C ABI against the float64 oracle's block-mask path, on
+seeded inputs and seeded masks: ragged shapes, shared and per-head masks, rows
+and key blocks nobody sees, causal on top, and the full-size workload on sampled
+heads."""
+import math
+
+import numpy as np
+import pytest
+
+import io_aware_exact_02_amd as fa
+from io_aware_exact_02_amd import inputs as I
+from oracle import naive
+from tests.gpu_util import TOL_GRAD, TOL_LSE, TOL_O, draw, maxabs, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1), (100, 100), (300, 300), (1000, 1000), (257, 513), (513, 257), (640, 130)]
+
+
+def _mask(H, Tq, Tk, density, seed, per_head, empty_rows=(), keep_diagonal=False):
+    m = I.block_mask(H if per_head else 1, Tq, Tk, density, seed, keep_diagonal, empty_rows)
+    return m, torch().from_numpy(m).cuda()
+
+
+def _grad_tol(ref):
+    """The gradient bound holds for gradients of unit scale; a mask that leaves a row only
+    a few keys (a ragged last key block) makes P large and dS with it, and the bf16
+    rounding of dS before the dK, dV, dQ products grows in proportion: the bound scales
+    with the largest reference gradient when that exceeds 1."""
+    return TOL_GRAD["bf16"] * max(1.0, float(np.abs(ref).max()) if np.size(ref) else 1.0)
+
+
+def _check_lse(got, ref):
+    """lse within TOL_LSE where finite; rows without a visible key must be -inf on both sides."""
+    got = to_f64(got)
+    inf_r, inf_g = np.isneginf(ref), np.isneginf(got)
+    assert np.array_equal(inf_r, inf_g), int(np.sum(inf_r != inf_g))
+    assert maxabs(got[~inf_r], ref[~inf_r]) <= TOL_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("Tq,Tk", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_masked_forward_parity(d, Tq, Tk, causal, per_head):
+    B, H = 2, 3
+    dev, f = draw(B, H, Tq, Tk, d, "bf16", seed=3000 + Tq + 7 * Tk + d)
+    nq = -(-Tq // 128)
+    empty = (nq - 1,) if nq > 2 else ()
+    m, mt = _mask(H, Tq, Tk, 0.4, 3100 + Tq + Tk, per_head, empty_rows=empty)
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=causal)
+    torch().cuda.synchronize()
+    Or, Lr = naive.forward(f["q"], f["k"], f["v"], 1 / math.sqrt(d), causal, block_mask=m)
+    assert maxabs(to_f64(O), Or) <= TOL_O["bf16"]
+    _check_lse(lse, Lr)
+
+
+@pytest.mark.parametrize("grad", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Tq,Tk", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_backward_parity(grad, d, Tq, Tk, causal):
+    t = torch()
+    B, H = 2, 2
+    dev, f = draw(B, H, Tq, Tk, d, "bf16", seed=4000 + Tq + 7 * Tk + d, with_do=True)
+    nq = -(-Tq // 128)
+    empty = (1,) if nq > 2 else ()
+    m, mt = _mask(H, Tq, Tk, 0.45, 4100 + Tq + Tk, True, empty_rows=empty)
+    scale = 1 / math.sqrt(d)
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=causal)
+    gd = t.float32 if grad == "f32" else t.bfloat16
+    dQ, dK, dV = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, mt, causal=causal,
+                                    grad_dtype=gd)
+    t.cuda.synchronize()
+    rQ, rK, rV, _, _ = naive.backward(f["q"], f["k"], f["v"], f["do"], scale, causal, block_mask=m)
+    for got, ref, name in ((dQ, rQ, "dQ"), (dK, rK, "dK"), (dV, rV, "dV")):
+        g = to_f64(got)
+        assert np.isfinite(g).all(), name
+        assert maxabs(g, ref) <= _grad_tol(ref), name
+
+
+def test_all_ones_mask_is_the_dense_path_bit_for_bit():
+    """A mask that keeps every block visits the same tiles in the same order as fa_fwd / fa_bwd."""
+    t = torch()
+    B, H, Tq, Tk, d = 2, 2, 700, 600, 128
+    dev, _ = draw(B, H, Tq, Tk, d, "bf16", seed=4500, with_do=True)
+    mt = t.ones((1, -(-Tq // 128), -(-Tk // 128)), dtype=t.uint8, device="cuda")
+    for causal in (False, True):
+        O0, L0 = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal)
+        O1, L1 = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=causal)
+        g0 = fa.backward(dev["q"], dev["k"], dev["v"], O0, dev["do"], L0, causal=causal)
+        g1 = fa.backward_masked(dev["q"], dev["k"], dev["v"], O1, dev["do"], L1, mt, causal=causal)
+        t.cuda.synchronize()
+        assert t.equal(O0, O1) and t.equal(L0, L1), causal
+        for a, b in zip(g0, g1):
+            assert t.equal(a, b), causal
+
+
+def test_rows_and_keys_nobody_sees():
+    """An all-zero mask row: O = 0, lse = -inf, dQ = 0 exactly; a key block no kept row
+    sees: dK = dV = 0 exactly; an all-zero mask: everything zero, no NaN."""
+    t = torch()
+    B, H, Tq, Tk, d = 1, 2, 400, 520, 64
+    dev, _ = draw(B, H, Tq, Tk, d, "bf16", seed=4600, with_do=True)
+    m = np.ones((1, 4, 5), np.uint8)
+    m[0, 2, :] = 0                       # query rows 256..383 see nothing
+    m[0, :, 3] = 0                       # keys 384..511 are seen by nobody
+    mt = t.from_numpy(m).cuda()
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt)
+    dQ, dK, dV = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, mt)
+    t.cuda.synchronize()
+    assert t.all(O[:, :, 256:384] == 0) and t.all(t.isneginf(lse[:, :, 256:384]))
+    assert t.all(t.isfinite(lse[:, :, :256])) and t.all(t.isfinite(lse[:, :, 384:]))
+    assert t.all(dQ[:, :, 256:384] == 0)
+    assert t.all(dK[:, :, 384:512] == 0) and t.all(dV[:, :, 384:512] == 0)
+    for x in (O, dQ, dK, dV):
+        assert t.isfinite(x.float()).all()
+    z = t.zeros_like(mt)
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], z, causal=True)
+    dQ, dK, dV = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, z, causal=True)
+    t.cuda.synchronize()
+    assert t.all(O == 0) and t.all(t.isneginf(lse))
+    for x in (dQ, dK, dV):
+        assert t.all(x == 0)
+
+
+def test_causal_rows_whose_kept_blocks_lie_above_the_diagonal():
+    """Causal on top of a mask that keeps only blocks right of the diagonal for some rows:
+    those rows see no key (-inf, zeros), the rest match the oracle."""
+    t = torch()
+    B, H, T, d = 1, 1, 512, 128
+    dev, f = draw(B, H, T, T, d, "bf16", seed=4700, with_do=True)
+    m = np.zeros((1, 4, 4), np.uint8)
+    m[0, 0, 2] = 1                       # row block 0: only a block above the diagonal
+    m[0, 1, :2] = 1
+    m[0, 2, 3] = 1                       # row block 2: above the diagonal again
+    m[0, 3, [0, 3]] = 1
+    mt = t.from_numpy(m).cuda()
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=True)
+    dQ, dK, dV = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, mt, causal=True)
+    t.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    Or, Lr = naive.forward(f["q"], f["k"], f["v"], scale, True, block_mask=m)
+    rQ, rK, rV, _, _ = naive.backward(f["q"], f["k"], f["v"], f["do"], scale, True, block_mask=m)
+    assert maxabs(to_f64(O), Or) <= TOL_O["bf16"]
+    _check_lse(lse, Lr)
+    for got, ref in ((dQ, rQ), (dK, rK), (dV, rV)):
+        g = to_f64(got)
+        assert np.isfinite(g).all() and maxabs(g, ref) <= _grad_tol(ref)
+
+
+def test_masked_results_repeat_bit_for_bit():
+    t = torch()
+    B, H, T, d = 2, 4, 1100, 128
+    dev, _ = draw(B, H, T, T, d, "bf16", seed=4800, with_do=True)
+    _, mt = _mask(H, T, T, 0.5, 4801, True, keep_diagonal=True)
+    runs = []
+    for _ in range(2):
+        O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=True)
+        g = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, mt, causal=True)
+        runs.append((O, lse) + tuple(g))
+    t.cuda.synchronize()
+    for a, b in zip(*runs):
+        assert t.equal(a, b)
+
+
+def test_blocksparse_workload_sampled_heads():
+    """The block-sparse workload at full size (8 x 32 heads, T = 4096, d = 128, a
+    quarter of the blocks kept per head), forward and backward checked on whole
+    sampled heads."""
+    t = torch()
+    w = I.WORKLOADS["blocksparse_bf16_b8h32_t4096_d128_s25"]
+    dev, f = draw(w.B, w.H, w.Tq, w.Tk, w.d, w.dtype, w.seed, w.qk_spread, True)
+    m = I.workload_mask(w)
+    mt = t.from_numpy(m).cuda()
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=w.causal)
+    dQ, dK, dV = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, mt, causal=w.causal)
+    t.cuda.synchronize()
+    scale = 1 / math.sqrt(w.d)
+    for b, h in [(0, 0), (3, 17), (7, 31)]:
+        args = (f["q"][b, h], f["k"][b, h], f["v"][b, h])
+        Or, Lr = naive.forward_head(*args, scale, w.causal, block_mask=m[h])
+        assert maxabs(to_f64(O[b, h]), Or) <= TOL_O["bf16"], (b, h)
+        assert maxabs(to_f64(lse[b, h]), Lr) <= TOL_LSE, (b, h)
+        rQ, rK, rV = naive.backward_head(*args, f["do"][b, h], scale, w.causal, block_mask=m[h])[:3]
+        for got, ref, name in ((dQ, rQ, "dQ"), (dK, rK, "dK"), (dV, rV, "dV")):
+            assert maxabs(to_f64(got[b, h]), ref) <= _grad_tol(ref), (name, b, h)
