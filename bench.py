@@ -77,24 +77,47 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(w, raw, seconds: float):
-    """Time the float64 oracle's forward+backward on whole heads of the workload."""
+def mask_pairs(m, Tq: int, Tk: int, causal: bool):
+    """Visible (query, key) pairs per head under a block mask [heads][nqb][nkb] of
+    128 x 128 blocks (and the causal rule l <= r when asked for)."""
+    import numpy as np
+    nq, nk = m.shape[1], m.shape[2]
+    kstart = 128 * np.arange(nk)
+    kend = np.minimum(kstart + 128, Tk)
+    if causal:
+        r = np.arange(Tq)
+        cnt = np.clip(np.minimum(r[:, None] + 1, kend[None, :]) - kstart[None, :], 0, None)
+        blk = np.add.reduceat(cnt, 128 * np.arange(nq), axis=0)
+    else:
+        rows = np.minimum(128, Tq - 128 * np.arange(nq))
+        blk = rows[:, None] * (kend - kstart)[None, :]
+    return (np.asarray(m, np.int64) * blk[None]).sum(axis=(1, 2))
+
+
+def cpu_baseline(w, raw, seconds: float, bmask=None):
+    """Time the float64 oracle's forward+backward on whole heads of the workload
+    (with the workload's block mask when it has one)."""
     from oracle import naive
     from io_aware_exact_02_amd.inputs import as_f64
     cores = max(1, min(CPU_SHARE, os.cpu_count() or 1))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     scale = 1.0 / math.sqrt(w.d)
-    done, t_total = 0, 0.0
+    pairs = mask_pairs(bmask, w.Tq, w.Tk, w.causal) if bmask is not None else None
+    done, t_total, flops = 0, 0.0, 0.0
     while done < len(heads) and t_total < seconds:
         batch = heads[done:done + cores]
         bi, hi = [b for b, _ in batch], [h for _, h in batch]
         q, k, v, do = (as_f64(raw[x][bi, hi], w.dtype)[None] for x in ("q", "k", "v", "do"))
+        bm = None if bmask is None else bmask[hi]
         t0 = time.perf_counter()
-        naive.backward(q, k, v, do, scale, w.causal, workers=cores)
+        naive.backward(q, k, v, do, scale, w.causal, workers=cores, block_mask=bm)
         t_total += time.perf_counter() - t0
         done += len(batch)
+        if pairs is None:
+            flops += len(batch) / (w.B * w.H) * (w.flops_fwd() + w.flops_bwd())
+        else:
+            flops += 3.5 * 4.0 * w.d * float(sum(pairs[h] for h in hi))
         log(f"[cpu_baseline] {done} heads in {t_total:.1f} s")
-    flops = done / (w.B * w.H) * (w.flops_fwd() + w.flops_bwd())
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 NumPy oracle, forward+backward of {done} of {w.B * w.H} (batch, head) slices of "
                       f"the same workload (T={w.Tq}, d={w.d}, causal={w.causal}), {t_total:.1f} s on {cores} "
@@ -160,6 +183,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget (0 = skip)")
+    ap.add_argument("--density", type=float, default=None,
+                    help="block-sparse workloads: fraction of kept blocks (default: the workload's)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -171,7 +196,7 @@ def main(argv=None):
         return 2
     import torch
     import io_aware_exact_02_amd as fa
-    from io_aware_exact_02_amd.inputs import WORKLOADS, draw_workload
+    from io_aware_exact_02_amd.inputs import WORKLOADS, draw_workload, workload_mask
 
     w = WORKLOADS[a.workload]
     if w.Tq <= 32 and w.dtype == "bf16" and not w.backward:
@@ -199,15 +224,26 @@ def main(argv=None):
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     phases = [fa.FA_BWD_PRE, fa.FA_BWD_MAIN, fa.FA_BWD_POST]
+    bmask_np = bmask = None
+    if w.mask_density is not None:
+        bmask_np = workload_mask(w, a.density)
+        bmask = torch.from_numpy(bmask_np).to(dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, stream=stream)
+        if bmask is None:
+            fa.fa_fwd(q, k, v, o, lse, causal=w.causal, stream=stream)
+        else:
+            fa.fa_fwd_masked(q, k, v, o, lse, bmask, causal=w.causal, stream=stream)
         for i, ph in enumerate(phases):
             if ev is not None:
                 ev[i + 1].record(stream)
-            fa.fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, ws, ph, causal=w.causal, stream=stream)
+            if bmask is None:
+                fa.fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, ws, ph, causal=w.causal, stream=stream)
+            else:
+                fa.fa_bwd_masked_phases(q, k, v, o, do, lse, dq, dk, dv, bmask, ws, ph, causal=w.causal,
+                                        stream=stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -235,6 +271,9 @@ def main(argv=None):
     dur = {n: sum(events[s][i].elapsed_time(events[s][i + 1]) for s in range(a.steps)) / a.steps
            for i, n in enumerate(names)}
     f_fwd, f_bwd = w.flops_fwd(), w.flops_bwd()
+    if bmask_np is not None:                    # kept pairs only: 4 d per visible (query, key) pair
+        f_fwd = 4.0 * d * B * float(mask_pairs(bmask_np, Tq, Tk, w.causal).sum())
+        f_bwd = 2.5 * f_fwd
     total = f_fwd + f_bwd
     value = total / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -262,7 +301,7 @@ def main(argv=None):
     cpu = None
     if a.cpu_seconds > 0:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(w, raw, a.cpu_seconds)
+        cpu = cpu_baseline(w, raw, a.cpu_seconds, bmask_np)
     out = {
         "metric": METRIC if w.name == DEFAULT_WORKLOAD else f"attention fwd+bwd TFLOP/s ({w.name})",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -273,6 +312,10 @@ def main(argv=None):
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
+    if bmask_np is not None:
+        out["config"].update(block_mask="seeded Bernoulli per 128 x 128 block, one per head, diagonal kept",
+                             kept_blocks=round(float(bmask_np.mean()), 4),
+                             flops="4 d per kept (query, key) pair forward, 2.5 x that backward")
     print(json.dumps(out), flush=True)
     return 0
 

@@ -172,8 +172,8 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
  * dV = 0.  bfloat16 inputs only; the backward takes d in {64, 128}.  Other
  * arguments, layouts, workspace and outputs as fa_fwd / fa_bwd.  Errors as
  * those, plus FA_ERR_NULL for a missing mask, FA_ERR_SHAPE for mask_heads not
- * in {1, H} or more than 32768 blocks along Tq or Tk, FA_ERR_DTYPE for float32
- * inputs and FA_ERR_HEADDIM for a d = 256 backward.  Results repeat bit for bit.
+ * in {1, H}, FA_ERR_DTYPE for float32 inputs and FA_ERR_HEADDIM for a d = 256
+ * backward.  Results repeat bit for bit.
  */
 int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* lse,
                   int B, int H, int Tq, int Tk, int d, float scale, int causal,
@@ -184,6 +184,14 @@ int fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, co
                   int B, int H, int Tq, int Tk, int d, float scale, int causal,
                   int dtype, int o_dtype, int grad_dtype, const unsigned char* block_mask,
                   int mask_heads, void* workspace, size_t workspace_bytes, void* stream);
+/* fa_bwd_masked split into phases, as fa_bwd_phases splits fa_bwd (same bits,
+ * order, workspace contract and FA_ERR_PHASE). */
+int fa_bwd_masked_phases(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* lse, void* dQ, void* dK, void* dV,
+                         int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                         int dtype, int o_dtype, int grad_dtype, const unsigned char* block_mask,
+                         int mask_heads, void* workspace, size_t workspace_bytes, int phases,
+                         void* stream);
 
 /* Static, human-readable text for an fa_status value (never NULL). */
 const char* fa_strerror(int status);

@@ -23,7 +23,7 @@ __all__ = [
     "FA_F32", "FA_BF16", "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_POST", "FA_BWD_ALL", "FAError", "LIB_PATH", "library", "fa_fwd", "fa_bwd",
     "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "forward_splitkv", "fa_fwd_masked", "fa_bwd_masked",
-    "forward_masked", "backward_masked", "MASK_BLOCK", "EXPORTED_SYMBOLS",
+    "fa_bwd_masked_phases", "forward_masked", "backward_masked", "MASK_BLOCK", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32 = 0
@@ -31,7 +31,7 @@ FA_BF16 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror",
                     "fa_abi_version", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_masked",
-                    "fa_bwd_masked")
+                    "fa_bwd_masked", "fa_bwd_masked_phases")
 MASK_BLOCK = 128          # block-mask granularity, in query rows and in keys
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST, FA_BWD_ALL = 1, 2, 4, 7
 
@@ -73,6 +73,8 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_masked.restype = i
     lib.fa_bwd_masked.argtypes = lib.fa_bwd.argtypes[:19] + [vp, i, vp, sz, vp]
     lib.fa_bwd_masked.restype = i
+    lib.fa_bwd_masked_phases.argtypes = lib.fa_bwd.argtypes[:19] + [vp, i, vp, sz, i, vp]
+    lib.fa_bwd_masked_phases.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     _lib = lib
@@ -246,6 +248,13 @@ def fa_fwd_masked(q, k, v, o, lse, block_mask, *, scale=None, causal=False, stre
 def fa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace, *, scale=None, causal=False,
                   stream=None) -> None:
     """Block-sparse backward (bf16 inputs, d in {64, 128}) into caller-provided dq, dk, dv."""
+    fa_bwd_masked_phases(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace, FA_BWD_ALL, scale=scale,
+                         causal=causal, stream=stream)
+
+
+def fa_bwd_masked_phases(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace, phases, *, scale=None,
+                         causal=False, stream=None) -> None:
+    """The named phases of the block-sparse backward (an OR of FA_BWD_PRE, _MAIN, _POST)."""
     torch = _torch()
     B, H, Tq, d = q.shape
     Tk = k.shape[2]
@@ -263,13 +272,13 @@ def fa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace, *, sca
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     c = 1.0 / math.sqrt(d) if scale is None else float(scale)
     nbytes = workspace.numel() * workspace.element_size()
-    st = library().fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk, d, c,
-                                 int(bool(causal)), _dtype_code(q), _dtype_code(o), _dtype_code(dq),
-                                 block_mask.data_ptr(), mh, workspace.data_ptr(), nbytes,
-                                 _stream_handle(stream, dev))
+    st = library().fa_bwd_masked_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk,
+                                        d, c, int(bool(causal)), _dtype_code(q), _dtype_code(o), _dtype_code(dq),
+                                        block_mask.data_ptr(), mh, workspace.data_ptr(), nbytes, int(phases),
+                                        _stream_handle(stream, dev))
     if st != 0:
-        raise FAError(st, "fa_bwd_masked")
+        raise FAError(st, "fa_bwd_masked_phases")
 
 
 def forward(q, k, v, *, causal=False, scale=None, out_dtype=None, stream=None):

@@ -26,13 +26,11 @@ int check_common(int B, int H, int Tq, int Tk, int d, float scale, int dtype) {
   return FA_OK;
 }
 
-// block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)] bytes; the kernels keep a
-// mask row or column as a bitmap of at most 32768 bits in LDS
-int check_mask(const unsigned char* block_mask, int mask_heads, int H, int Tq, int Tk, int dtype) {
+// block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)] bytes
+int check_mask(const unsigned char* block_mask, int mask_heads, int H, int dtype) {
   if (!block_mask) return FA_ERR_NULL;
   if (mask_heads != 1 && mask_heads != H) return FA_ERR_SHAPE;
   if (dtype != FA_BF16) return FA_ERR_DTYPE;
-  if ((Tq + 127) / 128 > 32768 || (Tk + 127) / 128 > 32768) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -108,7 +106,7 @@ int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* l
   if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
-  st = check_mask(block_mask, mask_heads, H, Tq, Tk, dtype);
+  st = check_mask(block_mask, mask_heads, H, dtype);
   if (st != FA_OK) return st;
   if (!valid_dtype(out_dtype)) return FA_ERR_DTYPE;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse)) return FA_ERR_ALIGN;
@@ -116,13 +114,22 @@ int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* l
                              static_cast<hipStream_t>(stream), block_mask, mask_heads);
 }
 
+int fa_bwd_masked_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                         const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d,
+                         float scale, int causal, int dtype, int o_dtype, int grad_dtype,
+                         const unsigned char* block_mask, int mask_heads, void* workspace, size_t workspace_bytes,
+                         int phases, void* stream) {
+  if (!block_mask) return FA_ERR_NULL;
+  return bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype, grad_dtype,
+                  block_mask, mask_heads, workspace, workspace_bytes, phases, stream);
+}
+
 int fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                   void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                   int dtype, int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads,
                   void* workspace, size_t workspace_bytes, void* stream) {
-  if (!block_mask) return FA_ERR_NULL;
-  return bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype, grad_dtype,
-                  block_mask, mask_heads, workspace, workspace_bytes, FA_BWD_ALL, stream);
+  return fa_bwd_masked_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype,
+                              grad_dtype, block_mask, mask_heads, workspace, workspace_bytes, FA_BWD_ALL, stream);
 }
 
 }  // extern "C"
@@ -137,7 +144,7 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
   if (block_mask) {
-    st = check_mask(block_mask, mask_heads, H, Tq, Tk, dtype);
+    st = check_mask(block_mask, mask_heads, H, dtype);
     if (st != FA_OK) return st;
     if (d == 256) return FA_ERR_HEADDIM;
   }

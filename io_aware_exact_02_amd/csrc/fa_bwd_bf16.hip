@@ -445,13 +445,13 @@ struct KvLayout {
 };
 
 // Block-sparse sweeps ([ZtF] "Dropout, block-sparsity, and other real-kernel
-// details"): the mask holds one byte per (128-query block, 128-key block); a
-// key block's workgroup first gathers its mask column into an LDS bitmap (bit r
-// = query block r may attend to it) and then visits only the query tiles whose
-// block bit is set.  Each role walks the same tile sequence with its own cursor,
-// so both still pass the same number of barriers.
+// details"): the mask holds one byte per (128-query block, 128-key block).  A
+// key block's workgroup visits only the query tiles whose block keeps it; each
+// wave reads its mask column 64 blocks at a time as a bit word (a ballot, held
+// in scalar registers) and walks the visible tiles with its own cursor.  Every
+// wave derives the same sequence, so both roles pass the same number of
+// barriers.
 constexpr int kMaskBlock = 128;
-constexpr int kVisWords = 512;                  // bitmap words: up to 32768 query blocks
 constexpr int kTilesPerMaskRow = kMaskBlock / kBQ;
 static_assert(kBKC == kMaskBlock, "one key-block workgroup per mask column");
 
@@ -463,7 +463,6 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk) {
   using L = KvLayout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-  __shared__ unsigned long long vis[MASKED ? kVisWords : 1];
 
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
@@ -486,19 +485,26 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   // visible query tiles: all from it0 on, or (masked) those whose block bit is set
   const int nmq = (Tq + kMaskBlock - 1) / kMaskBlock;
   const int nvw = (nmq + 63) >> 6;
-  auto vis_word = [&](int w) {
-    const unsigned long long x = vis[w];
-    return ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32)) << 32) |
-           __builtin_amdgcn_readfirstlane((unsigned)x);
+  const uint8_t* mcol = MASKED ? bmask + (long long)(bh % H) * mask_hstride + kblk : nullptr;
+  // bit r of word w: query block 64w + r keeps this key block.  The word last
+  // read is kept; a cursor moving forward reads again only every 64 blocks.
+  int cw = -1;
+  unsigned long long cbits = 0;
+  auto word = [&](int w) {
+    if (w != cw) {
+      cw = w;
+      cbits = mask_word(mcol, nmk, nmq, w, lane);
+    }
+    return cbits;
   };
-  auto vis_row = [&](int r) { return ((vis_word(r >> 6) >> (r & 63)) & 1ull) != 0; };
+  auto vis_row = [&](int r) { return ((word(r >> 6) >> (r & 63)) & 1ull) != 0; };
   auto next_row = [&](int r) {                  // first visible query block >= r, nmq if none
     int w = r >> 6;
     if (w >= nvw) return nmq;
-    unsigned long long bits = vis_word(w) & (~0ull << (r & 63));
+    unsigned long long bits = word(w) & (~0ull << (r & 63));
     while (bits == 0) {
       if (++w >= nvw) return nmq;
-      bits = vis_word(w);
+      bits = word(w);
     }
     return w * 64 + (int)__builtin_ctzll(bits);
   };
@@ -514,18 +520,11 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   };
   int n = nqt - it0;                            // query tiles in the sweep
   if constexpr (MASKED) {
-    const uint8_t* mcol = bmask + (long long)(bh % H) * mask_hstride + kblk;
-    for (int w = wave; w < nvw; w += 8) {
-      const int r = w * 64 + lane;
-      const unsigned long long bits = __ballot(r < nmq && mcol[(long long)r * nmk] != 0);
-      if (lane == 0) vis[w] = bits;
-    }
-    __syncthreads();
     n = 0;
     if (it0 < nqt) {
       const int rlo = it0 / kTilesPerMaskRow;
       for (int w = rlo >> 6; w < nvw; ++w) {
-        unsigned long long bits = vis_word(w);
+        unsigned long long bits = word(w);
         if (w == (rlo >> 6)) bits &= ~0ull << (rlo & 63);
         n += __builtin_popcountll(bits);
       }
@@ -827,7 +826,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   constexpr int BC = L::BC;
   static_assert(kMaskBlock % BC == 0 && kDqBR == 2 * kMaskBlock, "two mask rows, whole tiles per mask block");
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
-  __shared__ unsigned long long vis[MASKED ? 2 * kVisWords : 1];
 
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
@@ -914,34 +912,33 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
 
-  // ---- visible key tiles
+  // ---- visible key tiles: bit c of word w of mask row a (b) = key block
+  // 64w + c is kept for the first (second) 128 queries.  The words last read
+  // are kept; a cursor moving forward reads again only every 64 key blocks.
   const int nvw = (nmk + 63) >> 6;
-  auto vis_word = [&](int w) {
-    const unsigned long long x = vis[w];
-    return ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(x >> 32)) << 32) |
-           __builtin_amdgcn_readfirstlane((unsigned)x);
-  };
-  if constexpr (MASKED) {
-    const int mr = q0 / kMaskBlock;
-    const bool has_b = mr + 1 < (Tq + kMaskBlock - 1) / kMaskBlock;
-    const uint8_t* m = bmask + (long long)(bh % H) * mask_hstride + (long long)mr * nmk;
-    for (int i = wave; i < 2 * nvw; i += kDqWaves) {
-      const int row = i / nvw, w = i - row * nvw;
-      const int c = w * 64 + lane;
-      const unsigned long long bits = __ballot(c < nmk && (row == 0 || has_b) && m[(long long)row * nmk + c] != 0);
-      if (lane == 0) vis[row * kVisWords + w] = bits;
+  const int mr = q0 / kMaskBlock;
+  const bool has_b = mr + 1 < (Tq + kMaskBlock - 1) / kMaskBlock;
+  const uint8_t* mrow = MASKED ? bmask + (long long)(bh % H) * mask_hstride + (long long)mr * nmk : nullptr;
+  int cw = -1;
+  unsigned long long ca = 0, cb = 0;
+  auto words = [&](int w) {
+    if (w != cw) {
+      cw = w;
+      ca = mask_word(mrow, 1, nmk, w, lane);
+      cb = has_b ? mask_word(mrow + nmk, 1, nmk, w, lane) : 0ull;
     }
-    __syncthreads();
-  }
+  };
   auto next_tile = [&](int j) {                       // first tile >= j either mask row sees, ntile if none
     if constexpr (MASKED) {
       if (j >= ntile) return ntile;
       const int c = j * BC / kMaskBlock;
       int w = c >> 6;
-      unsigned long long bits = (vis_word(w) | vis_word(kVisWords + w)) & (~0ull << (c & 63));
+      words(w);
+      unsigned long long bits = (ca | cb) & (~0ull << (c & 63));
       while (bits == 0) {
         if (++w >= nvw) return ntile;
-        bits = vis_word(w) | vis_word(kVisWords + w);
+        words(w);
+        bits = ca | cb;
       }
       const int c2 = w * 64 + (int)__builtin_ctzll(bits);
       return c2 == c ? j : min(ntile, c2 * (kMaskBlock / BC));
@@ -952,7 +949,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   auto wave_sees = [&](int j) {                       // this wave's mask row sees tile j
     if constexpr (MASKED) {
       const int c = j * BC / kMaskBlock;
-      return ((vis_word((wave >> 2) * kVisWords + (c >> 6)) >> (c & 63)) & 1ull) != 0;
+      words(c >> 6);
+      return ((((wave >> 2) ? cb : ca) >> (c & 63)) & 1ull) != 0;
     } else {
       return true;
     }
@@ -969,10 +967,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   // tile j in stage ST (the step's parity in the sweep); jn is the tile after it
   auto step = [&](int j, int jn, auto stage) {
     constexpr int ST = decltype(stage)::value;
+    // the mask test comes before the loads of block jn: a branch between those
+    // loads and the reads of stage ST would make the compiler wait for the loads
+    const bool sees = wave_sees(j);
     t_load(first_row(jn));
     kv_dma(first_row(jn), ST ^ 1);
     const int kt0 = j * BC;
-    if ((!CAUSAL || kt0 <= qw + 31) && wave_sees(j)) {   // some key of the block is visible to this wave
+    if ((!CAUSAL || kt0 <= qw + 31) && sees) {          // some key of the block is visible to this wave
       const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk);
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb) {
@@ -1112,7 +1113,6 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
   // block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)]
   const int nmq = (Tq + kMaskBlock - 1) / kMaskBlock, nmk = (Tk + kMaskBlock - 1) / kMaskBlock;
   const long long mhs = mask_heads == 1 ? 0 : (long long)nmq * nmk;
-  if (bmask && (nmq > 64 * kVisWords || nmk > 64 * kVisWords)) return FA_ERR_SHAPE;
   if constexpr (D == 256) {
     if (bmask) return FA_ERR_HEADDIM;
     // one key-block sweep that also adds dQ contributions into a float32 accumulator

@@ -101,4 +101,13 @@ __device__ __forceinline__ void sched_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
 }
 
+// Bits 64w .. 64w+63 of a byte mask, as one 64-bit word that is the same in
+// every lane (bit i set iff m[(64w + i) * stride] != 0; entries at or past n
+// read as 0).  A ballot puts it straight into scalar registers: one load per
+// lane, no LDS and no barrier.  Call it with the whole wave active.
+__device__ __forceinline__ unsigned long long mask_word(const uint8_t* m, long long stride, int n, int w, int lane) {
+  const int i = w * 64 + lane;
+  return __ballot(i < n && m[(long long)i * stride] != 0);
+}
+
 }  // namespace fa

@@ -211,15 +211,32 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // Key blocks the sweep visits: all of them, or (block mask, [ZtF] "Dropout,
   // block-sparsity, and other real-kernel details") only those whose 128-key
   // mask block is kept for this 128-row block; next_tile(j) is the first
-  // visited block at or after j (ntile when none is left).
+  // visited block at or after j (ntile when none is left).  The mask row is
+  // read 64 blocks at a time as a bit word held in scalar registers.
   static_assert(kBR == 128 && 128 % BC == 0, "one mask row per query block, whole key blocks per mask block");
   const uint8_t* mrow = MASKED ? bmask + (bh % H) * mask_hstride + (long long)qb * nmk : nullptr;
+  const int nvw = (nmk + 63) >> 6;
+  int cw = -1;
+  unsigned long long cbits = 0;
+  auto word = [&](int w) {
+    if (w != cw) {
+      cw = w;
+      cbits = mask_word(mrow, 1, nmk, w, lane);
+    }
+    return cbits;
+  };
   auto next_tile = [&](int j) {
     if constexpr (MASKED) {
-      // the byte is the same for every lane: readfirstlane keeps the loop wave-uniform
-      while (j < ntile && __builtin_amdgcn_readfirstlane(mrow[(j * BC) >> 7]) == 0)
-        j = ((((j * BC) >> 7) + 1) << 7) / BC;
-      return j < ntile ? j : ntile;
+      if (j >= ntile) return ntile;
+      const int c = (j * BC) >> 7;
+      int w = c >> 6;
+      unsigned long long bits = word(w) & (~0ull << (c & 63));
+      while (bits == 0) {
+        if (++w >= nvw) return ntile;
+        bits = word(w);
+      }
+      const int c2 = w * 64 + (int)__builtin_ctzll(bits);
+      return c2 == c ? j : min(ntile, (c2 << 7) / BC);
     } else {
       return j;
     }

@@ -130,6 +130,7 @@ def block_mask(heads, Tq, Tk, density, seed, keep_diagonal=True, empty_rows=()):
     return m
 
 
-def workload_mask(w: Workload):
-    """The block mask of a block-sparse workload: one per head, seeded from the workload."""
-    return block_mask(w.H, w.Tq, w.Tk, w.mask_density, w.seed + 1000)
+def workload_mask(w: Workload, density=None):
+    """The block mask of a block-sparse workload: one per head, seeded from the workload
+    (`density` overrides the workload's own, for sweeps)."""
+    return block_mask(w.H, w.Tq, w.Tk, w.mask_density if density is None else density, w.seed + 1000)

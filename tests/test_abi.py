@@ -196,10 +196,16 @@ def test_masked_argument_errors(lib):
     assert _mbwd(lib, d=256) == HEADDIM           # the forward takes d = 256, the backward does not
     assert _mfwd(lib, d=96) == HEADDIM
     assert _mfwd(lib, Tq=0) == SHAPE
-    # more than 32768 mask blocks along a sequence (d = 64 keeps the size check of a slice happy)
-    assert _mfwd(lib, Tk=32768 * 128 + 1, d=64) == SHAPE
-    assert _mbwd(lib, Tq=32768 * 128 + 1, d=64) == SHAPE
     assert _mbwd(lib, ws=None) == WORKSPACE
     need = fa.fa_bwd_workspace_bytes(1, 2, 300, 300, 128, fa.FA_BF16, fa.FA_BF16)
     assert _mbwd(lib, ws_bytes=need - 1) == WORKSPACE
     assert _mbwd(lib, ws=P + 8, ws_bytes=need) == ALIGN
+
+
+def test_masked_phase_mask(lib):
+    args = [P] * 9 + [1, 2, 300, 300, 128, 0.125, 0, fa.FA_BF16, fa.FA_BF16, fa.FA_BF16, P, 1, P, 1 << 30]
+    assert lib.fa_bwd_masked_phases(*args, 8, None) == PHASE
+    assert lib.fa_bwd_masked_phases(*args, 0, None) == OK         # checks only, launches nothing
+    bad = list(args)
+    bad[19] = None
+    assert lib.fa_bwd_masked_phases(*bad, 0, None) == NULL

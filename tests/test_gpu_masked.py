@@ -150,6 +150,33 @@ def test_causal_rows_whose_kept_blocks_lie_above_the_diagonal():
         assert np.isfinite(g).all() and maxabs(g, ref) <= _grad_tol(ref)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_masks_wider_than_one_bitmap_word(causal):
+    """66 x 66 blocks (T = 8392): the kernels keep a mask row or column as 64-bit words.
+    Block 31 (the top bit of a word's low half) is kept while blocks 40-59 are dropped,
+    so a word read that smeared bit 31 into the high half would visit dropped tiles."""
+    t = torch()
+    B, H, T, d = 1, 1, 64 * 128 + 200, 64
+    dev, f = draw(B, H, T, T, d, "bf16", seed=4900, with_do=True)
+    m = I.block_mask(1, T, T, 0.3, 4901, keep_diagonal=True)
+    m[:, 31, :] = 1
+    m[:, :, 31] = 1
+    m[:, 40:60, :] = 0
+    m[:, :, 40:60] = 0
+    mt = t.from_numpy(m).cuda()
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=causal)
+    dQ, dK, dV = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, mt, causal=causal)
+    t.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    args = (f["q"][0, 0], f["k"][0, 0], f["v"][0, 0])
+    rQ, rK, rV, rO, rL, _ = naive.backward_head(*args, f["do"][0, 0], scale, causal, block_mask=m[0])
+    assert maxabs(to_f64(O[0, 0]), rO) <= TOL_O["bf16"]
+    _check_lse(lse[0, 0], rL)
+    for got, ref, name in ((dQ, rQ, "dQ"), (dK, rK, "dK"), (dV, rV, "dV")):
+        assert maxabs(to_f64(got[0, 0]), ref) <= _grad_tol(ref), name
+    assert t.all(dQ[0, 0, 40 * 128:60 * 128] == 0) and t.all(dK[0, 0, 40 * 128:60 * 128] == 0)
+
+
 def test_masked_results_repeat_bit_for_bit():
     t = torch()
     B, H, T, d = 2, 4, 1100, 128
