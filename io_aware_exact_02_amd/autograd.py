@@ -9,13 +9,19 @@ calls into autograd (no arithmetic of its own, no fallback).
     import io_aware_exact_02_amd.autograd as faa
     out = faa.attention(q, k, v, causal=True)     # q, k, v: [B, H, T, d] bf16/fp32 on the GPU
     out.sum().backward()                            # fills q.grad, k.grad, v.grad
+
+A `block_mask` (uint8 [1 or H, ceil(Tq/128), ceil(Tk/128)] on the GPU) restricts
+attention to the kept 128 x 128 blocks ([ZtF] "Dropout, block-sparsity, and other
+real-kernel details"); both passes then run the block-sparse kernels.
 """
 from __future__ import annotations
 
 import torch
 
 from . import backward as _fa_backward
+from . import backward_masked as _fa_backward_masked
 from . import forward as _fa_forward
+from . import forward_masked as _fa_forward_masked
 
 __all__ = ["FlashAttentionFunction", "attention"]
 
@@ -24,21 +30,30 @@ class FlashAttentionFunction(torch.autograd.Function):
     """O = softmax(scale Q K^T [causal mask]) V; lse is kept for the backward pass."""
 
     @staticmethod
-    def forward(ctx, q, k, v, causal: bool, scale):
+    def forward(ctx, q, k, v, causal: bool, scale, block_mask=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, lse = _fa_forward(q, k, v, causal=causal, scale=scale)
-        ctx.save_for_backward(q, k, v, o, lse)
-        ctx.causal, ctx.scale = causal, scale
+        if block_mask is None:
+            o, lse = _fa_forward(q, k, v, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+        else:
+            o, lse = _fa_forward_masked(q, k, v, block_mask, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, o, lse, block_mask)
+        ctx.causal, ctx.scale, ctx.masked = causal, scale, block_mask is not None
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse = ctx.saved_tensors
+        q, k, v, o, lse = ctx.saved_tensors[:5]
         do = do.to(q.dtype).contiguous()
-        dq, dk, dv = _fa_backward(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale)
-        return dq, dk, dv, None, None
+        if ctx.masked:
+            dq, dk, dv = _fa_backward_masked(q, k, v, o, do, lse, ctx.saved_tensors[5], causal=ctx.causal,
+                                             scale=ctx.scale)
+        else:
+            dq, dk, dv = _fa_backward(q, k, v, o, do, lse, causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None, None
 
 
-def attention(q, k, v, *, causal: bool = False, scale=None):
-    """Differentiable exact attention over [B, H, T, d] tensors (scale defaults to 1/sqrt(d))."""
-    return FlashAttentionFunction.apply(q, k, v, bool(causal), scale)
+def attention(q, k, v, *, causal: bool = False, scale=None, block_mask=None):
+    """Differentiable exact attention over [B, H, T, d] tensors (scale defaults to 1/sqrt(d)),
+    optionally restricted to the kept blocks of `block_mask`."""
+    return FlashAttentionFunction.apply(q, k, v, bool(causal), scale, block_mask)

@@ -59,3 +59,24 @@ def test_attention_autograd_respects_scale_and_second_use():
         assert np.isfinite(to_f64(q.grad)).all()
         for got, ref in ((q.grad, rQ), (k.grad, rK), (v.grad, rV)):
             assert maxabs(to_f64(got), ref) <= TOL_GRAD["bf16"]
+
+
+def test_attention_autograd_with_block_mask_matches_direct_calls():
+    """With a block mask the wrapper runs the block-sparse kernels: same bits as calling
+    fa_fwd_masked / fa_bwd_masked directly."""
+    import io_aware_exact_02_amd as fa
+    import io_aware_exact_02_amd.autograd as faa
+    from io_aware_exact_02_amd import inputs as I
+    t = torch()
+    B, H, T, d = 2, 2, 700, 128
+    dev, _ = draw(B, H, T, T, d, "bf16", seed=8200, with_do=True)
+    mt = t.from_numpy(I.block_mask(H, T, T, 0.5, 8201, keep_diagonal=True)).cuda()
+    q, k, v = (dev[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    out = faa.attention(q, k, v, causal=True, block_mask=mt)
+    out.backward(dev["do"])
+    O, lse = fa.forward_masked(dev["q"], dev["k"], dev["v"], mt, causal=True)
+    dQ, dK, dV = fa.backward_masked(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, mt, causal=True)
+    t.cuda.synchronize()
+    assert t.equal(out.detach(), O)
+    for got, ref in ((q.grad, dQ), (k.grad, dK), (v.grad, dV)):
+        assert t.equal(got, ref)
