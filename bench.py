@@ -279,11 +279,7 @@ def main(argv=None):
     peak = PEAK_TFLOPS[w.dtype]
     # FLOPs of the tile products each kernel forms (2 d per visible pair each):
     # the key-block sweep forms S, dP, dV, dK; the query-block sweep S, dP, dQ.
-    # The 256-wide bf16 backward forms all five in its key-block sweep.
-    fused = w.dtype == "bf16" and d == 256
-    kflops = {"fwd": f_fwd, "bwd_main": f_bwd if fused else 0.8 * f_bwd}
-    if not fused:
-        kflops["bwd_post"] = 0.6 * f_bwd
+    kflops = {"fwd": f_fwd, "bwd_main": 0.8 * f_bwd, "bwd_post": 0.6 * f_bwd}
     kernels = {}
     for n in names:
         entry = {"ms": round(dur[n], 4)}
@@ -293,7 +289,7 @@ def main(argv=None):
         kernels[n] = entry
     dom = max(kflops, key=lambda n: dur[n])
     ach = kflops[dom] / (dur[dom] * 1e-3) / 1e12
-    kernel_name = {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_bf16_w4_kernel" if fused else "bwd_kv_kernel",
+    kernel_name = {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_kv_w4_kernel" if d == 256 else "bwd_kv_kernel",
                    "bwd_post": "bwd_dq_kernel"}[dom]
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": read_traffic(kernel_name, w.name),

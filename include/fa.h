@@ -58,11 +58,9 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 /* Phases of the backward pass, for fa_bwd_phases. */
 typedef enum {
   FA_BWD_PRE = 1,   /* row terms D = rowsum(dO * O) (and -lse log2 e) into the
-                       workspace; where a float32 dQ accumulator is used, clear it  */
-  FA_BWD_MAIN = 2,  /* key-block sweep: recompute P, write dK and dV (d = 256 with
-                       bf16 inputs: also add each block's dQ share to the accumulator) */
-  FA_BWD_POST = 4,  /* dQ: query-block sweep that recomputes P and writes dQ (d = 256
-                       with bf16 inputs: round the accumulator to the gradient dtype) */
+                       workspace                                                    */
+  FA_BWD_MAIN = 2,  /* key-block sweep: recompute P, write dK and dV                */
+  FA_BWD_POST = 4,  /* query-block sweep: recompute P, write dQ                     */
   FA_BWD_ALL = 7
 } fa_bwd_phase;
 
@@ -86,11 +84,9 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
 /*
  * Bytes of device workspace fa_bwd needs, all float32 and per query row
  * ([B][H][Tq], each array rounded up to a multiple of 64 entries): the row
- * terms D_r = dO_r . O_r ([ZtF] "The backward pass, derived", Observation 2)
- * -- for bf16 inputs with d <= 128 stored as -D_r next to -lse_r log2(e) --
- * and, for d = 256 with bf16 inputs and bf16 gradients, a float32 dQ
- * accumulator [B][H][Tq][d] that receives the per-key-block contributions
- * ("Which loop goes outside?").  Returns 0 for invalid arguments.
+ * terms D_r = dO_r . O_r ([ZtF] "The backward pass, derived", Observation 2),
+ * for bf16 inputs stored as -D_r next to -lse_r log2(e).  Returns 0 for
+ * invalid arguments.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, int grad_dtype);
 
@@ -101,9 +97,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, in
  * o_dtype and grad_dtype: the input dtype, or FA_F32 for bfloat16 inputs.
  * Two sweeps ([ZtF] "Which loop goes outside?"): one over key blocks writes dK
  * and dV, one over query blocks writes dQ; both recompute P from lse, and every
- * output is summed in a fixed order, so results repeat bit for bit.  The one
- * exception is d = 256 with bf16 inputs, where the key-block sweep adds its dQ
- * shares with float32 atomics and dQ may differ in its last bits between runs.
+ * output is summed in a fixed order, so results repeat bit for bit.
  * workspace: device buffer of at least fa_bwd_workspace_bytes(...) bytes,
  * 16-byte aligned, owned by the caller; its contents on entry do not matter.
  * Returns FA_OK or an fa_status error code.
@@ -120,8 +114,7 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
  * phases it names run in the order PRE, MAIN, POST on `stream`.  Running the
  * three in that order (in one call or several, with the same arguments and
  * workspace) is exactly fa_bwd.  MAIN and POST read the row terms PRE left in
- * the workspace; where a dQ accumulator is used, POST reads what MAIN added to
- * it.  Same arguments and errors as
+ * the workspace.  Same arguments and errors as
  * fa_bwd, plus FA_ERR_PHASE for bits outside FA_BWD_ALL; phases = 0 checks the
  * arguments and launches nothing.
  */
@@ -169,11 +162,10 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
  *   mask_heads  1 (one mask shared by all heads) or H (one per head)
  * A query row whose mask row keeps no key (or, causal, no key at or before it)
  * gets O = 0 and lse = -inf, and its dQ is 0; keys no kept row sees get dK =
- * dV = 0.  bfloat16 inputs only; the backward takes d in {64, 128}.  Other
+ * dV = 0.  bfloat16 inputs only.  Other
  * arguments, layouts, workspace and outputs as fa_fwd / fa_bwd.  Errors as
  * those, plus FA_ERR_NULL for a missing mask, FA_ERR_SHAPE for mask_heads not
- * in {1, H}, FA_ERR_DTYPE for float32 inputs and FA_ERR_HEADDIM for a d = 256
- * backward.  Results repeat bit for bit.
+ * in {1, H} and FA_ERR_DTYPE for float32 inputs.  Results repeat bit for bit.
  */
 int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* lse,
                   int B, int H, int Tq, int Tk, int d, float scale, int causal,

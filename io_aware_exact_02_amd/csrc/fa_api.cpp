@@ -78,10 +78,8 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* lse, int
 size_t fa_bwd_workspace_bytes(int B, int H, int Tq, int Tk, int d, int dtype, int grad_dtype) {
   if (check_common(B, H, Tq, Tk, d, 1.f, dtype) != FA_OK || !valid_dtype(grad_dtype)) return 0;
   const long long rows = (long long)B * H * Tq;
-  long long floats = fa::bwd_rows_padded(rows);                 // D (fp32 and 256-wide paths) or -D
-  if (dtype == FA_BF16 && d <= 128) floats += fa::bwd_rows_padded(rows);   // -lse log2 e
-  // only the 256-wide bf16 backward sums dQ in a float32 accumulator (bf16 gradients)
-  if (dtype == FA_BF16 && grad_dtype == FA_BF16 && d == 256) floats += rows * d;
+  long long floats = fa::bwd_rows_padded(rows);                 // D (fp32 inputs) or -D (bf16)
+  if (dtype == FA_BF16) floats += fa::bwd_rows_padded(rows);      // -lse log2 e
   return (size_t)floats * sizeof(float);
 }
 
@@ -146,7 +144,6 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
   if (block_mask) {
     st = check_mask(block_mask, mask_heads, H, dtype);
     if (st != FA_OK) return st;
-    if (d == 256) return FA_ERR_HEADDIM;
   }
   if (!valid_dtype(grad_dtype) || (dtype == FA_F32 && grad_dtype != FA_F32)) return FA_ERR_DTYPE;
   if (!valid_dtype(o_dtype) || (dtype == FA_F32 && o_dtype != FA_F32)) return FA_ERR_DTYPE;

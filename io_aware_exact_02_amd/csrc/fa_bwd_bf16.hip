@@ -7,36 +7,17 @@
 // pre-pass leaves in the workspace (Observation 2) and rebuilds the weights
 // from lse as P = exp2(S * scale*log2e - lse*log2e) (Observation 1).
 //
-// Head widths 64 and 128: two sweeps, no atomics, each output summed in a
-// fixed order.
-//   * bwd_kv_kernel: one workgroup per block of 128 keys sweeps the query
-//     blocks and writes dK_j and dV_j once.
-//   * bwd_dq_kernel: one workgroup per block of 256 queries sweeps the key
-//     blocks and writes dQ_i once.
-// The split costs two extra tile products (S and dP are formed in both sweeps)
-// but no dQ traffic beyond one write: adding each key block's share of dQ with
-// float32 atomics would send Tk/128 partial sums per dQ element through the
-// memory-side atomic units, which is slower on this part than recomputing.
-//
-// Head width 256 (bwd_bf16_w4_kernel): a single key-block sweep whose four
-// waves each own 32 keys and keep K_j, V_j (as MFMA B operands) and the float32
-// accumulators dK_j, dV_j in registers.  Per query block i:
-//   * Q_i and dO_i are read from HBM once (16-byte buffer loads, one block
-//     ahead, into registers) and written to LDS twice: row-major for the
-//     products that contract over the feature axis, and transposed (query
-//     order permuted to match the MFMA k-slots) for the ones that contract
-//     over queries.  lse_i (times log2 e) and D_i go to LDS as well.
-//   * S = Q_i K_j^T on MFMA with one key per lane; only blocks that cross the
-//     causal diagonal are masked.  Rows past Tq and keys past Tk need no mask:
-//     their Q/dO or K/V rows read as zeros, so they add nothing.
-//   * dV_j += P^T dO_i; dP = dO_i V_j^T; dS = P * (dP - D_i) (Observation 3);
-//     dK_j += dS^T Q_i -- all on MFMA with P and dS taken from registers.
-//   * dS (bf16) goes to LDS; after the block's barrier the workgroup forms
-//     dQ_i's contribution of all 128 keys, scale * dS K_j, and adds it to a
-//     float32 accumulator in HBM with buffer atomics (rows past Tq are dropped
-//     by the buffer range check).  The order in which different key blocks
-//     add is not fixed, so dQ's last bits may vary between runs.  A pre-pass
-//     clears the accumulator; a post-pass rounds it if the caller wants bf16.
+// Every head width: two sweeps, no atomics, each output summed in a fixed
+// order ([ZtF] "Which loop goes outside?"):
+//   * key-block sweep: one workgroup per block of 128 keys sweeps the query
+//     tiles and writes dK_j and dV_j once (bwd_kv_kernel for d = 64 and 128,
+//     bwd_kv_w4_kernel for d = 256);
+//   * query-block sweep (bwd_dq_kernel): one workgroup per block of queries
+//     sweeps the key blocks and writes dQ_i once.
+// The split forms S and dP twice (seven tile products instead of five) but
+// sends no dQ traffic beyond one write: adding each key block's share of dQ
+// with float32 atomics would send Tk/128 partial sums per dQ element through
+// the memory-side atomic units, which is slower on this part than recomputing.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -50,48 +31,136 @@ constexpr int kWavesB = 4;
 constexpr int kBKC = kKeysPerWave * kWavesB;   // keys per workgroup
 constexpr int kBQ = 32;                        // query rows per step
 
+// Block-sparse sweeps ([ZtF] "Dropout, block-sparsity, and other real-kernel
+// details"): the mask holds one byte per (128-query block, 128-key block).  A
+// key block's workgroup visits only the query tiles whose block keeps it; each
+// wave reads its mask column 64 blocks at a time as a bit word (a ballot, held
+// in scalar registers) and walks the visible tiles with its own cursor.  Every
+// wave derives the same sequence, so all waves pass the same number of
+// barriers.
+constexpr int kMaskBlock = 128;
+constexpr int kTilesPerMaskRow = kMaskBlock / kBQ;
+static_assert(kBKC == kMaskBlock, "one key-block workgroup per mask column");
+
+// The query tiles a key-block sweep visits, shared by both key-block kernels:
+// all tiles from it0 on, or (masked) those whose 128-query block keeps this key
+// block.  count() is their number, next(t) the first visible tile >= t (nqt
+// when none is left).  Every lane of the wave must be active in both.
+template <bool MASKED>
+struct KeyBlockTiles {
+  const uint8_t* mcol;     // mask column of this key block (stride nmk), MASKED only
+  int nmk, nmq, nvw, nqt, it0, lane;
+  int cw = -1;             // the word last read is kept in scalar registers
+  unsigned long long cbits = 0;
+
+  __device__ KeyBlockTiles(const uint8_t* bmask, long long head_off, int kblk, int nmk_, int Tq, int it0_, int lane_)
+      : mcol(MASKED ? bmask + head_off + kblk : nullptr), nmk(nmk_), nmq((Tq + kMaskBlock - 1) / kMaskBlock),
+        nvw((nmq + 63) >> 6), nqt((Tq + kBQ - 1) / kBQ), it0(it0_), lane(lane_) {}
+  // bit r of word w: query block 64w + r keeps this key block
+  __device__ unsigned long long word(int w) {
+    if (w != cw) {
+      cw = w;
+      cbits = mask_word(mcol, nmk, nmq, w, lane);
+    }
+    return cbits;
+  }
+  __device__ bool row(int r) { return ((word(r >> 6) >> (r & 63)) & 1ull) != 0; }
+  __device__ int next_row(int r) {               // first visible query block >= r, nmq if none
+    int w = r >> 6;
+    if (w >= nvw) return nmq;
+    unsigned long long bits = word(w) & (~0ull << (r & 63));
+    while (bits == 0) {
+      if (++w >= nvw) return nmq;
+      bits = word(w);
+    }
+    return w * 64 + (int)__builtin_ctzll(bits);
+  }
+  __device__ int next(int t) {
+    if constexpr (MASKED) {
+      if (t >= nqt) return nqt;
+      if (row(t / kTilesPerMaskRow)) return t;
+      const int r = next_row(t / kTilesPerMaskRow + 1);
+      return r < nmq ? r * kTilesPerMaskRow : nqt;
+    } else {
+      return t;
+    }
+  }
+  __device__ int count() {
+    if constexpr (MASKED) {
+      if (it0 >= nqt) return 0;
+      const int rlo = it0 / kTilesPerMaskRow;
+      int n = 0;
+      for (int w = rlo >> 6; w < nvw; ++w) {
+        unsigned long long bits = word(w);
+        if (w == (rlo >> 6)) bits &= ~0ull << (rlo & 63);
+        n += __builtin_popcountll(bits);
+      }
+      n *= kTilesPerMaskRow;
+      if (row(rlo)) n -= it0 - rlo * kTilesPerMaskRow;           // the first block starts at it0
+      if (row(nmq - 1)) n -= nmq * kTilesPerMaskRow - nqt;       // the last block is ragged
+      return n;
+    } else {
+      return nqt - it0;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Key-block sweep for d = 256 (bwd_kv_w4_kernel): dK_j and dV_j.
+//
+// Four waves, one per SIMD, each owning 32 keys: K_j, V_j (MFMA B operands)
+// and the float32 accumulators dK_j, dV_j stay in registers (the accumulators
+// alone take 256 per lane, so two waves per SIMD do not fit).  Per query tile
+// i of 32 rows, double-buffered in LDS:
+//   * Q_i and dO_i go HBM -> registers one tile ahead -> LDS twice: row-major
+//     for the products over features, and transposed (query order permuted to
+//     the MFMA k-slots) for the products over queries.  Ln_i and Dn_i (the
+//     negated row terms) go beside them.
+//   * S = Q_i K_j^T and dP = dO_i V_j^T with one key per lane; P = exp2(S c
+//     log2e + Ln_i) and dS = P (dP + Dn_i) ([ZtF] "The backward pass,
+//     derived", Observations 1-3); only tiles crossing the causal diagonal
+//     are masked.  Rows past Tq and keys past Tk read as zeros and add nothing.
+//   * dV_j += P^T dO_i and dK_j += dS^T Q_i with P and dS straight from
+//     registers.
+// dQ comes from the query-block sweep below, as for the narrower heads.
+// ---------------------------------------------------------------------------
 template <int D>
-struct BwdLayout {
-  static constexpr int NST = D == 256 ? 1 : 2;  // Q/dO/dS stages
+struct W4Layout {
   static constexpr int NSTR = D + 8;            // row-major tiles (bf16 per row)
-  static constexpr int TSTR = kBQ + 8;          // transposed Q/dO tiles: D rows of 32 queries
-  static constexpr int KTSTR = kBKC + 8;        // transposed K tile: D rows of 128 keys
-  static constexpr int SSTR = kBKC + 8;         // dS tile: 32 rows of 128 keys
-  // byte offsets inside one stage
-  static constexpr int Q_N = 0;
+  static constexpr int TSTR = kBQ + 8;          // transposed tiles: D rows of 32 queries
+  static constexpr int Q_N = 0;                 // byte offsets inside one stage
   static constexpr int Q_T = Q_N + kBQ * NSTR * 2;
   static constexpr int G_N = Q_T + D * TSTR * 2;
   static constexpr int G_T = G_N + kBQ * NSTR * 2;
-  static constexpr int L_F = G_T + D * TSTR * 2;       // lse * log2 e [32]
-  static constexpr int D_F = L_F + kBQ * 4;            // D [32]
+  static constexpr int L_F = G_T + D * TSTR * 2;       // Ln [32]
+  static constexpr int D_F = L_F + kBQ * 4;            // Dn [32]
   static constexpr int STAGE = D_F + kBQ * 4;
-  static constexpr int S_OFF = NST * STAGE;            // dS tiles
-  static constexpr int S_BYTES = kBQ * SSTR * 2;
-  static constexpr int KT_OFF = S_OFF + NST * S_BYTES; // K^T of the key block
-  static constexpr int BYTES = KT_OFF + D * KTSTR * 2;
+  static constexpr int BYTES = 2 * STAGE;
   static constexpr int NDS = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int NBLK = (kBQ / 8) * (D / 8);     // 8x8 blocks per tensor tile
-  static_assert(STAGE % 16 == 0 && S_BYTES % 16 == 0, "LDS regions must stay 16-byte aligned");
+  static_assert(STAGE % 16 == 0, "LDS regions must stay 16-byte aligned");
   static_assert(2 * ((NBLK + 63) / 64) <= 4, "Q and dO staging waves fit in the workgroup");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
-void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                     const float* __restrict__ lse, const float* __restrict__ Dr,
-                     float* __restrict__ dQacc, void* __restrict__ dK, void* __restrict__ dV,
-                     int Tq, int Tk, float scale, float cl2e, int nkb, int grad_f32) {
-  using L = BwdLayout<D>;
+void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                      const float* __restrict__ Ln, const float* __restrict__ Dn,
+                      void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e,
+                      int nkb, int grad_f32, const uint8_t* __restrict__ bmask, int H, long long mask_hstride,
+                      int nmk) {
+  using L = W4Layout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
   const int bh = lin / nkb;
   const int kblk = CAUSAL ? nkb - 1 - (lin % nkb) : (lin % nkb);   // causal: longest sweeps first
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
   const int k0 = kblk * kBKC;
@@ -102,9 +171,8 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
   const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
   const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
-  const rsrc_t rl = make_rsrc(lse + (size_t)bh * Tq, (unsigned)Tq * 4u);
-  const rsrc_t rd = make_rsrc(Dr + (size_t)bh * Tq, (unsigned)Tq * 4u);
-  const rsrc_t racc = make_rsrc(dQacc + qbase, (unsigned)Tq * D * 4u);
+  const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
+  const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
 
   // K_j and V_j as B operands (column = key, k = features), held for the sweep.
   bf16x8 kf[L::NDS], vf[L::NDS];
@@ -113,25 +181,6 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const unsigned off = ((unsigned)mykey * D + ds * 16 + 8 * hf) * 2u;
     kf[ds] = as_bf16x8(bload16(rk, off));
     vf[ds] = as_bf16x8(bload16(rv, off));
-  }
-  // K_j^T for the dQ product: 8x8 blocks (8 keys x 8 features) transposed into LDS
-  for (int b = tid; b < (kBKC / 8) * (D / 8); b += 256) {
-    const int kg = b % (kBKC / 8), dg = b / (kBKC / 8);
-    u32x4 r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = bload16(rk, ((unsigned)(k0 + kg * 8 + i) * D + dg * 8) * 2u);
-    char* kt = smem + L::KT_OFF + (dg * 8 * L::KTSTR + kg * 8) * 2;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u32x4 even, odd;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        even[p] = lo_lo(r[2 * p][w], r[2 * p + 1][w]);
-        odd[p] = hi_hi(r[2 * p][w], r[2 * p + 1][w]);
-      }
-      st16(kt + (2 * w) * L::KTSTR * 2, even);
-      st16(kt + (2 * w + 1) * L::KTSTR * 2, odd);
-    }
   }
 
   f32x16 dk[L::NDB], dv[L::NDB];
@@ -145,15 +194,17 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
   const int nqt = (Tq + kBQ - 1) / kBQ;
   const int it0 = CAUSAL ? min(k0 / kBQ, nqt) : 0;
+  KeyBlockTiles<MASKED> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  const int n = tiles.count();                  // query tiles in the sweep
 
-  // ---- staging of one query tile (Q_i, dO_i, lse_i, D_i) ----
+  // ---- staging of one query tile (Q_i, dO_i, Ln_i, Dn_i) ----
   // Whole waves stage one tensor each (so the buffer resource they load through
   // is wave-uniform): WPT waves per tensor, one 8x8 block (8 query rows x 8
   // features) per lane, features fastest across lanes so that a row-major store
-  // covers whole rows.  The top 32 threads also fetch lse and D.  A tile index
+  // covers whole rows.  The top 32 threads also fetch Ln and Dn.  A tile index
   // past the sweep maps to row Tq, whose loads return zeros.
   constexpr int WPT = (L::NBLK + 63) / 64;
-  const bool is_g = __builtin_amdgcn_readfirstlane(wave) >= WPT;
+  const bool is_g = wave >= WPT;
   const int tb = (wave % WPT) * 64 + lane;
   const bool tloader = wave < 2 * WPT && tb < L::NBLK;
   const rsrc_t rsrc_t_src = is_g ? rg : rq;
@@ -164,7 +215,7 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int srow = tid - (256 - kBQ);
   u32x4 stg[8];
   float sl = 0.f, sd = 0.f;
-  auto first_row = [&](int it) { return it < nqt ? it * kBQ : Tq; };
+  auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
   auto gload = [&](int r0) {
     if (tloader) {
 #pragma unroll
@@ -195,46 +246,24 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       }
     }
     if (sloader) {
-      reinterpret_cast<float*>(base + L::L_F)[srow] = sl * kLog2e;
+      reinterpret_cast<float*>(base + L::L_F)[srow] = sl;
       reinterpret_cast<float*>(base + L::D_F)[srow] = sd;
     }
   };
 
-  gload(first_row(it0));
+  int tc = tiles.next(it0);                     // the tile of the next step
+  gload(tile_row(tc));
   lstore(0);
   wait_vmem_all();
   __syncthreads();
 
-  // dQ atomics: lane = feature column, register r = query row 8(r/4)+4hf+r%4
-  auto dq_product = [&](int r0, const char* ss) {
-    for (int db = wave; db < L::NDB; db += kWavesB) {
-      f32x16 acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < kBKC / 16; ++ks) {
-        const bf16x8 a = as_bf16x8(ld16(ss + (l32 * L::SSTR + ks * 16 + 8 * hf) * 2));
-        const bf16x8 b =
-            as_bf16x8(ld16(smem + L::KT_OFF + ((db * 32 + l32) * L::KTSTR + ks * 16 + 8 * hf) * 2));
-        acc = mfma32(a, b, acc);
-      }
-      // the whole byte offset goes in the vector offset, which the range check
-      // covers: rows past Tq (whose contributions are zero anyway) are dropped
-      const unsigned vo = ((unsigned)(r0 + 4 * hf) * D + db * 32 + l32) * 4u;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(scale * acc[r], racc,
-                                                        vo + (unsigned)(8 * (r >> 2) + (r & 3)) * D * 4u, 0, 0);
-    }
-  };
-
-  auto step = [&](int it, auto stage) {
-    constexpr int ST = decltype(stage)::value;
-    constexpr int NX = L::NST == 2 ? (ST ^ 1) : 0;    // stage the next block is written to
-    const int r0 = it * kBQ;
+  // tile t in stage ST (the step's parity in the sweep); tn is the tile after it.
+  // One step per loop iteration with the stage as a run-time offset: two
+  // unrolled steps per iteration make the compiler spill the accumulators.
+  auto step = [&](int t, int tn, int ST) {
+    const int r0 = t * kBQ;
     const char* sb_ = smem + ST * L::STAGE;
-    char* ss = smem + L::S_OFF + ST * L::S_BYTES;
-    gload(first_row(it + 1));
+    gload(tile_row(tn));
 
     // S = Q_i K_j^T and dP = dO_i V_j^T: lane = key, register r = query 8(r/4)+4hf+r%4
     f32x16 s, dp;
@@ -250,6 +279,7 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
       dp = mfma32(g, vf[ds], dp);
     }
+    sched_reads_ahead<2 * L::NDS>();
     const float* lsv = reinterpret_cast<const float*>(sb_ + L::L_F);
     const float* dsv_ = reinterpret_cast<const float*>(sb_ + L::D_F);
     float p[16], dsv[16];
@@ -261,71 +291,48 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g4 + e;
-        p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, -lv[e]));
-        dsv[r] = dp[r] - dv4[e];
+        p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, lv[e]));
+        dsv[r] = dp[r] + dv4[e];
       }
     }
-    if (CAUSAL && r0 < kw0 + kKeysPerWave - 1) {       // block crosses this wave's diagonal
+    if (CAUSAL && r0 < kw0 + kKeysPerWave - 1) {       // the tile crosses this wave's diagonal
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
     }
     bf16x8 pb[2], sbf[2];
-    unsigned sw[8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t2 = 0; t2 < 2; ++t2) {
       u32x4 a, b;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 8 * t + 2 * e;
+        const int r = 8 * t2 + 2 * e;
         a[e] = pack_bf16(p[r], p[r + 1]);
         b[e] = pack_bf16(p[r] * dsv[r], p[r + 1] * dsv[r + 1]);
-        sw[4 * t + e] = b[e];
       }
-      pb[t] = as_bf16x8(a);
-      sbf[t] = as_bf16x8(b);
+      pb[t2] = as_bf16x8(a);
+      sbf[t2] = as_bf16x8(b);
     }
     // dV_j += P^T dO_i ; dK_j += dS^T Q_i  (lane = feature column, register = key row)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int db = 0; db < L::NDB; ++db) {
-        const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_T + ((db * 32 + l32) * L::TSTR + 16 * t + 8 * hf) * 2));
-        dv[db] = mfma32(pb[t], g, dv[db]);
-        const bf16x8 qq = as_bf16x8(ld16(sb_ + L::Q_T + ((db * 32 + l32) * L::TSTR + 16 * t + 8 * hf) * 2));
-        dk[db] = mfma32(sbf[t], qq, dk[db]);
+        const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_T + ((db * 32 + l32) * L::TSTR + 16 * t2 + 8 * hf) * 2));
+        dv[db] = mfma32(pb[t2], g, dv[db]);
+        const bf16x8 qq = as_bf16x8(ld16(sb_ + L::Q_T + ((db * 32 + l32) * L::TSTR + 16 * t2 + 8 * hf) * 2));
+        dk[db] = mfma32(sbf[t2], qq, dk[db]);
       }
-    // dS -> LDS as [query][key]: word k holds queries qr and qr+1 of this lane's key
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = 2 * k;
-      const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-      uint16_t* dst = reinterpret_cast<uint16_t*>(ss) + qr * L::SSTR + wave * kKeysPerWave + l32;
-      dst[0] = (uint16_t)(sw[k] & 0xffffu);
-      dst[L::SSTR] = (uint16_t)(sw[k] >> 16);
-    }
-    if (L::NST == 2) {
-      lstore(NX);
-      wait_vmem_all();
-      __syncthreads();
-      dq_product(r0, ss);
-    } else {
-      wait_vmem_all();
-      __syncthreads();
-      dq_product(r0, ss);
-      __syncthreads();
-      lstore(0);
-      __syncthreads();
-    }
+    sched_reads_ahead<4 * L::NDB>();
+    lstore(ST ^ 1);
+    wait_vmem_all();
+    __syncthreads();
   };
 
-  if (L::NST == 2) {
-    for (int it = it0; it < nqt; it += 2) {
-      step(it, std::integral_constant<int, 0>{});
-      if (it + 1 < nqt) step(it + 1, std::integral_constant<int, 1>{});
-    }
-  } else {
-    for (int it = it0; it < nqt; ++it) step(it, std::integral_constant<int, 0>{});
+  for (int s = 0; s < n; ++s) {
+    const int tn = tiles.next(tc + 1);
+    step(tc, tn, s & 1);
+    tc = tn;
   }
 
   // dK_j = scale * dS^T Q, dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
@@ -338,7 +345,8 @@ void bwd_bf16_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     for (int r = 0; r < 16; ++r) {
       const int key = kw0 + 8 * (r >> 2) + 4 * hf + (r & 3);
       const unsigned idx = (unsigned)key * D + db * 32 + l32;
-      const float gk = scale * dk[db][r], gv = dv[db][r];
+      const float gk = scale * dk[db][r];
+      const float gv = dv[db][r];   // a scalar copy: bit-casting a vector element in place reads element 0
       if (grad_f32) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gk), rdk, idx * 4u, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gv), rdv, idx * 4u, 0, 0);
@@ -444,17 +452,6 @@ struct KvLayout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Block-sparse sweeps ([ZtF] "Dropout, block-sparsity, and other real-kernel
-// details"): the mask holds one byte per (128-query block, 128-key block).  A
-// key block's workgroup visits only the query tiles whose block keeps it; each
-// wave reads its mask column 64 blocks at a time as a bit word (a ballot, held
-// in scalar registers) and walks the visible tiles with its own cursor.  Every
-// wave derives the same sequence, so both roles pass the same number of
-// barriers.
-constexpr int kMaskBlock = 128;
-constexpr int kTilesPerMaskRow = kMaskBlock / kBQ;
-static_assert(kBKC == kMaskBlock, "one key-block workgroup per mask column");
-
 template <int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -482,57 +479,10 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   // tile t covers query rows t kBQ ..; a tile past the sweep reads row Tq (zeros)
   auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
 
-  // visible query tiles: all from it0 on, or (masked) those whose block bit is set
-  const int nmq = (Tq + kMaskBlock - 1) / kMaskBlock;
-  const int nvw = (nmq + 63) >> 6;
-  const uint8_t* mcol = MASKED ? bmask + (long long)(bh % H) * mask_hstride + kblk : nullptr;
-  // bit r of word w: query block 64w + r keeps this key block.  The word last
-  // read is kept; a cursor moving forward reads again only every 64 blocks.
-  int cw = -1;
-  unsigned long long cbits = 0;
-  auto word = [&](int w) {
-    if (w != cw) {
-      cw = w;
-      cbits = mask_word(mcol, nmk, nmq, w, lane);
-    }
-    return cbits;
-  };
-  auto vis_row = [&](int r) { return ((word(r >> 6) >> (r & 63)) & 1ull) != 0; };
-  auto next_row = [&](int r) {                  // first visible query block >= r, nmq if none
-    int w = r >> 6;
-    if (w >= nvw) return nmq;
-    unsigned long long bits = word(w) & (~0ull << (r & 63));
-    while (bits == 0) {
-      if (++w >= nvw) return nmq;
-      bits = word(w);
-    }
-    return w * 64 + (int)__builtin_ctzll(bits);
-  };
-  auto next_tile = [&](int t) {                 // first visible tile >= t (nqt if none)
-    if constexpr (MASKED) {
-      if (t >= nqt) return nqt;
-      if (vis_row(t / kTilesPerMaskRow)) return t;
-      const int r = next_row(t / kTilesPerMaskRow + 1);
-      return r < nmq ? r * kTilesPerMaskRow : nqt;
-    } else {
-      return t;
-    }
-  };
-  int n = nqt - it0;                            // query tiles in the sweep
-  if constexpr (MASKED) {
-    n = 0;
-    if (it0 < nqt) {
-      const int rlo = it0 / kTilesPerMaskRow;
-      for (int w = rlo >> 6; w < nvw; ++w) {
-        unsigned long long bits = word(w);
-        if (w == (rlo >> 6)) bits &= ~0ull << (rlo & 63);
-        n += __builtin_popcountll(bits);
-      }
-      n *= kTilesPerMaskRow;
-      if (vis_row(rlo)) n -= it0 - rlo * kTilesPerMaskRow;          // first block starts at it0
-      if (vis_row(nmq - 1)) n -= nmq * kTilesPerMaskRow - nqt;      // last block is ragged
-    }
-  }
+  // visible query tiles: all from it0 on, or (masked) those whose block keeps this key block
+  KeyBlockTiles<MASKED> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  const int n = tiles.count();                  // query tiles in the sweep
+  auto next_tile = [&](int t) { return tiles.next(t); };
 
   if (wave < 4) {
     // ============================ score waves ============================
@@ -759,15 +709,17 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Query-block sweep for d = 64 and 128: dQ_i, in the other loop order ([ZtF]
-// "Which loop goes outside?"), so that each dQ row is summed in registers by
-// one wave and written once, with no atomics and a fixed summation order.
+// Query-block sweep: dQ_i, in the other loop order ([ZtF] "Which loop goes
+// outside?"), so that each dQ row is summed in registers by one wave and
+// written once, with no atomics and a fixed summation order.
 //
-// One workgroup of eight waves per (256-query block, b, h); each wave owns 32
-// query rows and keeps their Q and dO fragments (MFMA B operands), lse, D and
-// the float32 dQ^T accumulator in registers for a sweep over key blocks of 64
-// (causal: up to the block's last query; tiles a wave cannot see are skipped
-// by that wave).  Per key block j:
+// One workgroup per (query block, b, h): eight waves and 256 queries for d = 64
+// and 128, four waves (one per SIMD) and 128 queries for d = 256, where the Q
+// and dO fragments and the dQ^T accumulator alone take 256 registers per lane.
+// Each wave owns 32 query rows and keeps their Q and dO fragments (MFMA B
+// operands), lse, D and the float32 dQ^T accumulator in registers for a sweep
+// over key blocks of 64 keys (32 for d = 256) -- causal: up to the block's
+// last query; tiles a wave cannot see are skipped by that wave.  Per key block j:
 //   * K_j and V_j go HBM -> LDS by buffer_load ... lds (rows XOR-swizzled by
 //     16-byte chunk); K_j^T goes HBM -> registers -> LDS transposed, its key
 //     order matching the k-slot order of the dS fragments below.
@@ -778,13 +730,13 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 //   * dQ^T += K_j^T dS^T with dS^T rounded to bf16 straight from registers.
 // Epilogue: dQ = scale * dQ~, once, in the gradient dtype.
 // ---------------------------------------------------------------------------
-constexpr int kDqWaves = 8;
-constexpr int kDqBR = 32 * kDqWaves;          // query rows per workgroup
-constexpr int kDqBC = 64;                     // keys per block
-
 template <int D>
 struct DqLayout {
-  static constexpr int BC = kDqBC;
+  static constexpr int WAVES = D == 256 ? 4 : 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WAVES_PER_SIMD = WAVES / 4;
+  static constexpr int BR = 32 * WAVES;                // query rows per workgroup
+  static constexpr int BC = D == 256 ? 32 : 64;        // keys per block
   static constexpr int NC = D / 8;                     // 16-byte chunks per K/V row
   static constexpr int KST = BC * D * 2;               // K (or V) tile, swizzled rows, unpadded
   static constexpr int TSTR = BC + 8;                  // bf16 per K^T row (16-byte pad)
@@ -795,10 +747,10 @@ struct DqLayout {
   static constexpr int NDB = D / 32;
   static constexpr int NDS = D / 16;
   static constexpr int KDMA = KST / 1024;              // 1 KiB DMA instructions per K (or V) tile
-  static constexpr int KDMA_W = 2 * KDMA / kDqWaves;   // per wave: waves 0-3 load K, 4-7 load V
+  static constexpr int KDMA_W = 2 * KDMA / WAVES;      // per wave: the first half of the waves load K, the rest V
   static constexpr int NTB = (BC / 4) * (D / 8);       // 4 keys x 8 features blocks of K^T
-  static_assert((2 * KDMA) % kDqWaves == 0 && KDMA % (kDqWaves / 2) == 0, "DMA split over the waves");
-  static_assert(NTB <= 64 * kDqWaves, "one K^T block per thread at most");
+  static_assert((2 * KDMA) % WAVES == 0 && KDMA % (WAVES / 2) == 0, "DMA split over the waves");
+  static_assert(NTB <= THREADS, "one K^T block per thread at most");
   static_assert(NC == 8 || NC >= 16, "swizzle assumes 8 or >= 16 chunks per row");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
   static constexpr int k_off(int st) { return st * STAGE; }
@@ -817,14 +769,16 @@ __device__ __forceinline__ int dq_swz(int r) { return NC >= 16 ? (r & 15) : ((r 
 // workgroup visits the key tiles that either row can see, and a wave computes
 // only those its own row can see.
 template <int D, bool CAUSAL, bool MASKED>
-__global__ __launch_bounds__(512) void bwd_dq_kernel(
+__global__ __launch_bounds__(DqLayout<D>::THREADS)
+__attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
     void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32,
     const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk) {
   using L = DqLayout<D>;
   constexpr int BC = L::BC;
-  static_assert(kMaskBlock % BC == 0 && kDqBR == 2 * kMaskBlock, "two mask rows, whole tiles per mask block");
+  static_assert(kMaskBlock % BC == 0 && L::BR % kMaskBlock == 0 && L::BR <= 2 * kMaskBlock,
+                "one or two mask rows, whole tiles per mask block");
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   const int nblk = gridDim.x, wid = blockIdx.x;
@@ -835,7 +789,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
-  const int q0 = qb * kDqBR;
+  const int q0 = qb * L::BR;
   const int qw = q0 + wave * 32;
   const int myq = qw + lq;
 
@@ -862,10 +816,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   for (int r = 0; r < 16; ++r) dseed[r] = dnq;
 
   int ntile = (Tk + BC - 1) / BC;
-  if (CAUSAL) ntile = min(ntile, (min(q0 + kDqBR, Tq) - 1) / BC + 1);
+  if (CAUSAL) ntile = min(ntile, (min(q0 + L::BR, Tq) - 1) / BC + 1);
 
   // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled
-  const rsrc_t rkv = wave < kDqWaves / 2 ? rk : rv;
+  const rsrc_t rkv = wave < L::WAVES / 2 ? rk : rv;
   auto kv_dma = [&](int k0, int st) {
 #pragma unroll
     for (int i = 0; i < L::KDMA_W; ++i) {
@@ -917,7 +871,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   // are kept; a cursor moving forward reads again only every 64 key blocks.
   const int nvw = (nmk + 63) >> 6;
   const int mr = q0 / kMaskBlock;
-  const bool has_b = mr + 1 < (Tq + kMaskBlock - 1) / kMaskBlock;
+  const bool has_b = L::BR == 2 * kMaskBlock && mr + 1 < (Tq + kMaskBlock - 1) / kMaskBlock;
   const uint8_t* mrow = MASKED ? bmask + (long long)(bh % H) * mask_hstride + (long long)mr * nmk : nullptr;
   int cw = -1;
   unsigned long long ca = 0, cb = 0;
@@ -965,8 +919,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
   __syncthreads();
 
   // tile j in stage ST (the step's parity in the sweep); jn is the tile after it
-  auto step = [&](int j, int jn, auto stage) {
-    constexpr int ST = decltype(stage)::value;
+  auto step = [&](int j, int jn, int ST) {
     // the mask test comes before the loads of block jn: a branch between those
     // loads and the reads of stage ST would make the compiler wait for the loads
     const bool sees = wave_sees(j);
@@ -1035,20 +988,30 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     __syncthreads();
   };
 
-  if constexpr (MASKED) {
+  // The three loop forms compile differently; each is used where it needs no
+  // spills.  d <= 128 unrolls two steps so that every stage offset is a
+  // constant; d = 256 runs one step per iteration with the stage offset
+  // computed at run time.
+  if constexpr (D == 256) {
+    for (int j = j0, st = 0; j < ntile; st ^= 1) {
+      const int jn = next_tile(j + 1);
+      step(j, jn, st);
+      j = jn;
+    }
+  } else if constexpr (MASKED) {
     for (int j = j0; j < ntile;) {
       int jn = next_tile(j + 1);
-      step(j, jn, std::integral_constant<int, 0>{});
+      step(j, jn, 0);
       j = jn;
       if (j >= ntile) break;
       jn = next_tile(j + 1);
-      step(j, jn, std::integral_constant<int, 1>{});
+      step(j, jn, 1);
       j = jn;
     }
   } else {
     for (int j = 0; j < ntile; j += 2) {
-      step(j, j + 1, std::integral_constant<int, 0>{});
-      if (j + 1 < ntile) step(j + 1, j + 2, std::integral_constant<int, 1>{});
+      step(j, j + 1, 0);
+      if (j + 1 < ntile) step(j + 1, j + 2, 1);
     }
   }
 
@@ -1071,89 +1034,54 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(
     }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, long long n) {
-  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i + 3 < n) {
-    *reinterpret_cast<f32x4*>(p + i) = (f32x4){0.f, 0.f, 0.f, 0.f};
-  } else {
-    for (long long k = i; k < n; ++k) p[k] = 0.f;
-  }
-}
-
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
-                                                         long long n) {
-  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i + 3 < n) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
-    u32x2 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-    st8(dst + i, w);
-  } else {
-    for (long long k = i; k < n; ++k) dst[k] = (uint16_t)(pack_bf16(src[k], 0.f) & 0xffffu);
-  }
-}
-
 template <int D>
 int bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
         void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int o_f32, int grad_f32,
         void* workspace, int phases, hipStream_t stream, const uint8_t* bmask, int mask_heads) {
+  using LQ = DqLayout<D>;
   const long long rows = (long long)B * H * Tq;
-  const long long nq = rows * D;
   const int nkb = (Tk + kBKC - 1) / kBKC;
   const long long nblk = (long long)nkb * B * H;
-  const long long nfill = (nq + 1023) / 1024;
-  const int nqb = (Tq + kDqBR - 1) / kDqBR;
+  const int nqb = (Tq + LQ::BR - 1) / LQ::BR;
   const long long nqblk = (long long)nqb * B * H;
-  if (nblk > 0x7fffffffLL || nfill > 0x7fffffffLL || nqblk > 0x7fffffffLL) return FA_ERR_SHAPE;
+  constexpr int RPB = 256 / (D / 8);           // rows per row-terms block
+  const long long nrb = (rows + RPB - 1) / RPB;
+  if (nblk > 0x7fffffffLL || nqblk > 0x7fffffffLL || nrb > 0x7fffffffLL) return FA_ERR_SHAPE;
   const float cl2e = scale * kLog2e;
   auto q = static_cast<const uint16_t*>(Q);
   auto k = static_cast<const uint16_t*>(K);
   auto v = static_cast<const uint16_t*>(V);
   auto g = static_cast<const uint16_t*>(dO);
-  float* Dws = static_cast<float*>(workspace);
   // block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)]
   const int nmq = (Tq + kMaskBlock - 1) / kMaskBlock, nmk = (Tk + kMaskBlock - 1) / kMaskBlock;
   const long long mhs = mask_heads == 1 ? 0 : (long long)nmq * nmk;
-  if constexpr (D == 256) {
-    if (bmask) return FA_ERR_HEADDIM;
-    // one key-block sweep that also adds dQ contributions into a float32 accumulator
-    float* acc = grad_f32 ? static_cast<float*>(dQ) : Dws + bwd_rows_padded(rows);
-    if (phases & FA_BWD_PRE) {
-      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc, nq);
-      const int st = launch_rowdot_bf16(dO, O, o_f32, Dws, rows, D, stream);
-      if (st != FA_OK) return st;
-    }
-    if (phases & FA_BWD_MAIN) {
-      if (causal)
-        hipLaunchKernelGGL((bwd_bf16_w4_kernel<D, true>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g,
-                           lse, Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
-      else
-        hipLaunchKernelGGL((bwd_bf16_w4_kernel<D, false>), dim3((unsigned)nblk), dim3(256), 0, stream, q, k, v, g,
-                           lse, Dws, acc, dK, dV, Tq, Tk, scale, cl2e, nkb, grad_f32);
-    }
-    if ((phases & FA_BWD_POST) && !grad_f32)
-      hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)nfill), dim3(256), 0, stream, acc,
-                         static_cast<uint16_t*>(dQ), nq);
-  } else {
-    // key-block sweep for dK, dV; query-block sweep for dQ; both read the
-    // negated row terms Dn (workspace start) and Ln (after it)
-    float* Dn = Dws;
-    float* Ln = Dws + bwd_rows_padded(rows);
-    if (phases & FA_BWD_PRE) {
-      constexpr int RPB = 256 / (D / 8);
-      const long long nrb = (rows + RPB - 1) / RPB;
-      if (nrb > 0x7fffffffLL) return FA_ERR_SHAPE;
-      if (o_f32)
-        hipLaunchKernelGGL((row_terms_kernel<D, true>), dim3((unsigned)nrb), dim3(256), 0, stream, g, O, lse, Dn, Ln,
-                           rows);
-      else
-        hipLaunchKernelGGL((row_terms_kernel<D, false>), dim3((unsigned)nrb), dim3(256), 0, stream, g, O, lse, Dn, Ln,
-                           rows);
-    }
-    if (phases & FA_BWD_MAIN) {
-      auto kv = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3((unsigned)nblk), dim3(512), 0, stream, q, k, v, g, Ln, Dn, dK, dV, Tq, Tk,
-                           scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk);
-      };
+  // both sweeps read the negated row terms: Dn at the workspace start, Ln after it
+  float* Dn = static_cast<float*>(workspace);
+  float* Ln = Dn + bwd_rows_padded(rows);
+  if (phases & FA_BWD_PRE) {
+    if (o_f32)
+      hipLaunchKernelGGL((row_terms_kernel<D, true>), dim3((unsigned)nrb), dim3(256), 0, stream, g, O, lse, Dn, Ln,
+                         rows);
+    else
+      hipLaunchKernelGGL((row_terms_kernel<D, false>), dim3((unsigned)nrb), dim3(256), 0, stream, g, O, lse, Dn, Ln,
+                         rows);
+  }
+  if (phases & FA_BWD_MAIN) {
+    // key-block sweep: 8 waves in two roles for d <= 128, 4 waves for d = 256
+    constexpr int KV_THREADS = D == 256 ? 256 : 512;
+    auto kv = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)nblk), dim3(KV_THREADS), 0, stream, q, k, v, g, Ln, Dn, dK, dV, Tq,
+                         Tk, scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk);
+    };
+    if constexpr (D == 256) {
+      if (bmask) {
+        if (causal) kv(bwd_kv_w4_kernel<D, true, true>);
+        else kv(bwd_kv_w4_kernel<D, false, true>);
+      } else {
+        if (causal) kv(bwd_kv_w4_kernel<D, true, false>);
+        else kv(bwd_kv_w4_kernel<D, false, false>);
+      }
+    } else {
       if (bmask) {
         if (causal) kv(bwd_kv_kernel<D, true, true>);
         else kv(bwd_kv_kernel<D, false, true>);
@@ -1162,18 +1090,18 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
         else kv(bwd_kv_kernel<D, false, false>);
       }
     }
-    if (phases & FA_BWD_POST) {
-      auto dqk = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3((unsigned)nqblk), dim3(512), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq, Tk,
-                           scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk);
-      };
-      if (bmask) {
-        if (causal) dqk(bwd_dq_kernel<D, true, true>);
-        else dqk(bwd_dq_kernel<D, false, true>);
-      } else {
-        if (causal) dqk(bwd_dq_kernel<D, true, false>);
-        else dqk(bwd_dq_kernel<D, false, false>);
-      }
+  }
+  if (phases & FA_BWD_POST) {
+    auto dqk = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)nqblk), dim3(LQ::THREADS), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq,
+                         Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk);
+    };
+    if (bmask) {
+      if (causal) dqk(bwd_dq_kernel<D, true, true>);
+      else dqk(bwd_dq_kernel<D, false, true>);
+    } else {
+      if (causal) dqk(bwd_dq_kernel<D, true, false>);
+      else dqk(bwd_dq_kernel<D, false, false>);
     }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

@@ -24,11 +24,6 @@ namespace {
 constexpr int kTileKeys = 32;
 constexpr int kTileRows = 32;
 
-__device__ __forceinline__ float load_elem(const float* p) { return *p; }
-__device__ __forceinline__ float load_elem(const uint16_t* p) {
-  return __builtin_bit_cast(float, (unsigned)(*p) << 16);
-}
-
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
@@ -102,18 +97,18 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 // ------------------------------- D pre-pass --------------------------------
 // D_r = dO_r . O_r in float32 ([ZtF] "The backward pass, derived", Observation 2).
-template <int D, typename TG, typename TO>
-__global__ __launch_bounds__(256) void rowdot_kernel(const TG* __restrict__ dO, const TO* __restrict__ Ov,
+template <int D>
+__global__ __launch_bounds__(256) void rowdot_kernel(const float* __restrict__ dO, const float* __restrict__ Ov,
                                                     float* __restrict__ Dout, long long rows) {
   constexpr int G = 16, E = D / G;
   const long long r = (long long)blockIdx.x * (256 / G) + threadIdx.x / G;
   const int j = threadIdx.x % G;
   float part = 0.f;
   if (r < rows) {
-    const TG* a = dO + r * D;
-    const TO* b = Ov + r * D;
+    const float* a = dO + r * D;
+    const float* b = Ov + r * D;
 #pragma unroll
-    for (int e = 0; e < E; ++e) part = __builtin_fmaf(load_elem(a + e * G + j), load_elem(b + e * G + j), part);
+    for (int e = 0; e < E; ++e) part = __builtin_fmaf(a[e * G + j], b[e * G + j], part);
   }
   part = group_sum<G>(part);
   if (r < rows && j == 0) Dout[r] = part;
@@ -265,7 +260,7 @@ int bwd_f32(const float* Q, const float* K, const float* V, const float* Ov, con
   const long long nq = (long long)nqb * B * H, nk = (long long)nkb * B * H;
   if (nrd > 0x7fffffffLL || nq > 0x7fffffffLL || nk > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (phases & FA_BWD_PRE)
-    hipLaunchKernelGGL((rowdot_kernel<D, float, float>), dim3((unsigned)nrd), dim3(256), 0, stream, dO, Ov, Dws, rows);
+    hipLaunchKernelGGL((rowdot_kernel<D>), dim3((unsigned)nrd), dim3(256), 0, stream, dO, Ov, Dws, rows);
   if (phases & FA_BWD_MAIN) {   // key-block sweep: dK, dV
     if (causal)
       hipLaunchKernelGGL((bwd_kv_f32_kernel<D, true>), dim3((unsigned)nk), dim3(256), 0, stream, Q, K, V, dO, lse,
@@ -319,31 +314,6 @@ int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, c
     case 256: return bwd_f32<256>(q, k, v, o, g, lse, dq, dk, dv, B, H, Tq, Tk, scale, causal, ws, phases, stream);
     default: return FA_ERR_HEADDIM;
   }
-}
-
-template <int D>
-void rowdot_bf16(const uint16_t* g, const void* o, int o_f32, float* Dout, long long rows, unsigned nrd,
-                 hipStream_t stream) {
-  if (o_f32)
-    hipLaunchKernelGGL((rowdot_kernel<D, uint16_t, float>), dim3(nrd), dim3(256), 0, stream, g,
-                       static_cast<const float*>(o), Dout, rows);
-  else
-    hipLaunchKernelGGL((rowdot_kernel<D, uint16_t, uint16_t>), dim3(nrd), dim3(256), 0, stream, g,
-                       static_cast<const uint16_t*>(o), Dout, rows);
-}
-
-int launch_rowdot_bf16(const void* dO, const void* O, int o_f32, float* Dout, long long rows, int d,
-                       hipStream_t stream) {
-  const long long nrd = (rows + 15) / 16;
-  if (nrd > 0x7fffffffLL) return FA_ERR_SHAPE;
-  auto g = static_cast<const uint16_t*>(dO);
-  switch (d) {
-    case 64: rowdot_bf16<64>(g, O, o_f32, Dout, rows, (unsigned)nrd, stream); break;
-    case 128: rowdot_bf16<128>(g, O, o_f32, Dout, rows, (unsigned)nrd, stream); break;
-    case 256: rowdot_bf16<256>(g, O, o_f32, Dout, rows, (unsigned)nrd, stream); break;
-    default: return FA_ERR_HEADDIM;
-  }
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace fa

@@ -28,7 +28,5 @@ int splitkv_parts(int B, int H, int Tq, int Tk, int nsplit);
 int launch_decode_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
                        int Tk, int d, float scale, int causal, int out_f32, int nsplit, void* workspace,
                        hipStream_t stream);
-int launch_rowdot_bf16(const void* dO, const void* O, int o_f32, float* Dout, long long rows, int d,
-                       hipStream_t stream);
 
 }  // namespace fa

@@ -80,12 +80,11 @@ def test_bwd_workspace_bytes(lib):
     B, H, Tq, Tk, d = 2, 3, 100, 70, 128
     rows = B * H * Tq
     pad = (rows + 63) // 64 * 64
-    # bf16, d <= 128: two row-term arrays (-D and -lse log2 e); d = 256: D, plus the float32 dQ
-    # accumulator when the gradients are bf16; float32 inputs: D
-    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 8 * pad
-    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_BF16, fa.FA_F32) == 8 * pad
-    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 256, fa.FA_BF16, fa.FA_BF16) == 4 * (pad + rows * 256)
-    assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 256, fa.FA_BF16, fa.FA_F32) == 4 * pad
+    # bf16: two row-term arrays (-D and -lse log2 e), for every head width and gradient
+    # dtype; float32 inputs: D
+    for dd in (64, 128, 256):
+        assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, dd, fa.FA_BF16, fa.FA_BF16) == 8 * pad
+        assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, dd, fa.FA_BF16, fa.FA_F32) == 8 * pad
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, d, fa.FA_F32, fa.FA_F32) == 4 * pad
     assert fa.fa_bwd_workspace_bytes(0, H, Tq, Tk, d, fa.FA_BF16, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_bytes(B, H, Tq, Tk, 96, fa.FA_BF16, fa.FA_BF16) == 0
@@ -193,7 +192,7 @@ def test_masked_argument_errors(lib):
     assert _mfwd(lib, dtype=fa.FA_F32, odtype=fa.FA_F32) == DTYPE
     assert _mbwd(lib, dtype=fa.FA_F32) == DTYPE
     assert _mfwd(lib, odtype=7) == DTYPE
-    assert _mbwd(lib, d=256) == HEADDIM           # the forward takes d = 256, the backward does not
+    assert _mbwd(lib, d=96) == HEADDIM
     assert _mfwd(lib, d=96) == HEADDIM
     assert _mfwd(lib, Tq=0) == SHAPE
     assert _mbwd(lib, ws=None) == WORKSPACE

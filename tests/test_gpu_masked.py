@@ -57,7 +57,7 @@ def test_masked_forward_parity(d, Tq, Tk, causal, per_head):
 
 
 @pytest.mark.parametrize("grad", ["bf16", "f32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("Tq,Tk", SHAPES)
 @pytest.mark.parametrize("causal", [False, True])
 def test_masked_backward_parity(grad, d, Tq, Tk, causal):
