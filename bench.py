@@ -94,12 +94,49 @@ def mask_pairs(m, Tq: int, Tk: int, causal: bool):
     return (np.asarray(m, np.int64) * blk[None]).sum(axis=(1, 2))
 
 
+ORACLE_HEAD_BYTES = 1 << 30                     # largest T x T float64 matrix timed on whole heads
+
+
+def cpu_baseline_rows(w, raw, seconds: float, cores: int):
+    """For heads too large for the oracle's backward (its T x T matrices): time the
+    oracle's forward on sampled query rows, one head per thread."""
+    import numpy as np
+    from oracle import naive
+    from io_aware_exact_02_amd.inputs import as_f64
+    scale = 1.0 / math.sqrt(w.d)
+    rng = np.random.default_rng(w.seed)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    nrows = max(1, (ORACLE_HEAD_BYTES // 8) // w.Tk // cores)     # rows per head, all threads together ~1 GiB
+    done, rounds, t_total, flops = 0, 0, 0.0, 0.0
+    while t_total < seconds and rounds < 16:
+        batch = [heads[(done + i) % len(heads)] for i in range(cores)]
+        bi, hi = [b for b, _ in batch], [h for _, h in batch]
+        q, k, v = (as_f64(raw[x][bi, hi], w.dtype)[None] for x in ("q", "k", "v"))
+        rows = np.sort(rng.choice(w.Tq, size=min(nrows, w.Tq), replace=False))
+        t0 = time.perf_counter()
+        naive.forward(q, k, v, scale, w.causal, rows=rows, workers=cores)
+        t_total += time.perf_counter() - t0
+        pairs = float(np.sum(np.minimum(rows + 1, w.Tk))) if w.causal else float(len(rows)) * w.Tk
+        flops += 4.0 * w.d * pairs * len(batch)
+        done += len(batch)
+        rounds += 1
+        log(f"[cpu_baseline] {rounds} rounds of {len(batch)} heads x {len(rows)} rows in {t_total:.1f} s")
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 NumPy oracle, forward only, {rounds} rounds of {cores} (batch, head) slices x "
+                      f"{nrows} random query rows of the same workload (T={w.Tq}, d={w.d}, causal={w.causal}), "
+                      f"{t_total:.1f} s on {cores} threads with one BLAS thread each; its backward needs whole "
+                      f"T x T matrices per head ({w.Tq * w.Tk * 8 / 2**30:.0f} GiB each in float64), so only the "
+                      f"forward is timed; FLOPs counted as for the GPU"}
+
+
 def cpu_baseline(w, raw, seconds: float, bmask=None):
     """Time the float64 oracle's forward+backward on whole heads of the workload
     (with the workload's block mask when it has one)."""
     from oracle import naive
     from io_aware_exact_02_amd.inputs import as_f64
     cores = max(1, min(CPU_SHARE, os.cpu_count() or 1))
+    if w.Tq * w.Tk * 8 > ORACLE_HEAD_BYTES and bmask is None:
+        return cpu_baseline_rows(w, raw, seconds, cores)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     scale = 1.0 / math.sqrt(w.d)
     pairs = mask_pairs(bmask, w.Tq, w.Tk, w.causal) if bmask is not None else None

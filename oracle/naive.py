@@ -51,7 +51,7 @@ import numpy as np
 
 __all__ = [
     "scores_head", "probs_head", "forward_head", "backward_head",
-    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK",
+    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK", "dq_rows",
 ]
 
 MASK_BLOCK = 128   # side of a block-mask block, in query rows and in keys
@@ -143,6 +143,21 @@ def backward_head(q, k, v, do, scale, causal, block_mask=None):
     dQ = scale * (dS @ k)
     dK = scale * (dS.T @ q)
     return dQ, dK, dV, O, lse, D
+
+
+def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None):
+    """dQ[rows] of one head by the same chain rule ([ZtF] "The backward pass,
+    derived"): row r of dQ = c dS_r K needs only row r of P, of dP = dO V^T and
+    D_r = dO_r . O_r, so sampled rows are exact without the T x T matrices."""
+    rows = np.asarray(rows)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do_r = np.asarray(do, dtype=np.float64)[rows]
+    P, _ = probs_head(q, k, scale, causal, rows, block_mask)
+    O = P @ v
+    D = np.sum(do_r * O, axis=1)
+    dS = P * (do_r @ v.T - D[:, None])
+    return scale * (dS @ k)
 
 
 def _heads(B, H, heads):

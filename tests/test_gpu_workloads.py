@@ -91,6 +91,49 @@ def test_causal_bf16_b1h24_t65536_d256_forward_sampled_rows():
     assert torch().isfinite(O).all() and torch().isfinite(lse).all()
 
 
+def test_d256_backward_whole_heads_t4096():
+    """The d = 256 backward (key-block sweep plus dQ sweep) on whole heads of T = 4096,
+    causal and not, against the oracle element by element."""
+    t = torch()
+    B, H, T, d = 1, 2, 4096, 256
+    dev, f = draw(B, H, T, T, d, "bf16", seed=9256, with_do=True)
+    scale = 1 / math.sqrt(d)
+    for causal in (True, False):
+        O, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal)
+        dQ, dK, dV = fa.backward(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, causal=causal)
+        t.cuda.synchronize()
+        for h in range(H):
+            rQ, rK, rV = naive.backward_head(f["q"][0, h], f["k"][0, h], f["v"][0, h], f["do"][0, h], scale,
+                                             causal)[:3]
+            for got, ref, name in ((dQ, rQ, "dQ"), (dK, rK, "dK"), (dV, rV, "dV")):
+                err = maxabs(to_f64(got[0, h]), ref)
+                assert err <= TOL_GRAD["bf16"], (causal, name, h, err)
+
+
+def test_causal_bf16_b1h24_t65536_d256_backward_sampled_rows():
+    """The d = 256 backward at full size (24 heads x 65536): dQ on sampled rows against
+    the oracle (a dQ row needs only its own row of P, dP and D), and dV through an exact
+    identity: rows of P sum to 1, so sum_l dV_l = sum_r dO_r.  With P rounded to bf16
+    before the dV product each row's weights sum to 1 within 2^-9, which bounds the
+    difference by 2^-9 sum_r |dO_r| (plus float32 summation slack)."""
+    t = torch()
+    w, dev, f = _inputs("causal_bf16_b1h24_t65536_d256", True)
+    O, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=True)
+    dQ, dK, dV = fa.backward(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, causal=True, grad_dtype=t.float32)
+    t.cuda.synchronize()
+    assert t.isfinite(dQ).all() and t.isfinite(dK).all() and t.isfinite(dV).all()
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 32768, w.Tq - 1], rng.integers(0, w.Tq, 26)]))
+    scale = 1 / math.sqrt(w.d)
+    dv_sum = dV.sum(dim=2, dtype=t.float64).cpu().numpy()
+    for b, h in _heads(w, 2, 7):
+        ref = naive.dq_rows(f["q"][b, h], f["k"][b, h], f["v"][b, h], f["do"][b, h], scale, True, rows)
+        assert maxabs(to_f64(dQ[b, h][rows]), ref) <= TOL_GRAD["bf16"], (b, h)
+    do = f["do"]
+    bound = (2.0 ** -9 + 1e-5) * np.abs(do).sum(axis=2) + 1e-3
+    assert np.all(np.abs(dv_sum - do.sum(axis=2)) <= bound)
+
+
 def test_cross_bf16_b16h16_tq1024_tk8192_d128_forward_and_backward():
     """Q, K ~ N(0, 9): peaked softmax with large logits.
 

@@ -316,3 +316,28 @@ def test_batched_matches_per_head_and_rows_subset():
     Os, Ls = naive.forward(Q, K, V, 0.5, True, heads=[(1, 2)], rows=rows)
     assert np.allclose(Os[1, 2], O[1, 2][rows], atol=1e-15)
     assert np.isnan(Os[0, 0]).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_by_finite_differences(causal):
+    """dq_rows pinned by central differences of L = sum(O * dO) in q[r, j]: a change of
+    query r moves only row r of O, so the difference needs the forward of that row alone."""
+    rng = np.random.default_rng(90)
+    Tq, Tk, d, c = 40, 37, 5, 0.6
+    q, k, v, do = (rng.standard_normal(sh) for sh in ((Tq, d), (Tk, d), (Tk, d), (Tq, d)))
+    rows = np.array([0, 7, 23, 39])
+    got = naive.dq_rows(q, k, v, do, c, causal, rows)
+    h = 1e-6
+    for i, r in enumerate(rows):
+        for j in range(d):
+            p, m = q.copy(), q.copy()
+            p[r, j] += h
+            m[r, j] -= h
+            Op, _ = naive.forward_head(p, k, v, c, causal, rows=np.array([r]))
+            Om, _ = naive.forward_head(m, k, v, c, causal, rows=np.array([r]))
+            fd = float(np.sum((Op - Om)[0] * do[r])) / (2 * h)
+            assert abs(fd - got[i, j]) <= 1e-7 * (1 + abs(fd)), (r, j, fd, got[i, j])
+    # and it is the same rows of the whole-head backward (block mask included)
+    bm = np.array([[1]], np.uint8)
+    full = naive.backward_head(q, k, v, do, c, causal, block_mask=bm)[0]
+    assert np.allclose(naive.dq_rows(q, k, v, do, c, causal, rows, block_mask=bm), full[rows], atol=1e-13)
