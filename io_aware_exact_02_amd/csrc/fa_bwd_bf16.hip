@@ -431,9 +431,16 @@ __global__ __launch_bounds__(256) void row_terms_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvLayout {
-  static constexpr int NSTR = D + 8;            // row-major Q_i / dO_i (bf16 per row)
+  // Row-major Q_i / dO_i tiles: 16-byte chunk c of query row r sits at
+  // (r % 4) NB + (8 c + r / 4) 16.  A staging store (rows 4 qa + i, chunk fg,
+  // lane = 8 fg + qa) then covers consecutive 16-byte slots, and the 16 lanes of
+  // a score-wave read (rows r0 .. r0 + 15, one chunk) fall in 16 distinct bank
+  // groups thanks to the 64-byte pad between the four row classes.  The read of
+  // k-step ds sits at the lane's base + 256 ds.  (With plain rows of D + 8 bf16
+  // the staging stores conflicted.)
+  static constexpr int NB = 16 * D + 64;        // bytes of one row class (r % 4)
   static constexpr int TSTR = kBQ + 8;          // transposed tiles: D rows of 32 queries
-  static constexpr int N_BYTES = kBQ * NSTR * 2;
+  static constexpr int N_BYTES = 4 * NB;
   static constexpr int T_BYTES = D * TSTR * 2;
   static constexpr int Q_N = 0;                              // one stage: Q_i and dO_i row-major
   static constexpr int G_N = Q_N + N_BYTES;
@@ -513,6 +520,8 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         }
       }
     };
+    // this lane's row-major operand reads: query row l32, chunk 2 ds + hf (layout in KvLayout)
+    const int n_lane = (l32 & 3) * L::NB + (8 * hf + (l32 >> 2)) * 16;
     f32x16 lt0, dt0, lt1, dt1;
     int tc = next_tile(it0);                      // the tile of the next score step
     terms_load(tc, lt0, dt0);
@@ -532,8 +541,8 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       bf16x8 qa[L::NDS], ga[L::NDS];
 #pragma unroll
       for (int ds = 0; ds < L::NDS; ++ds) {
-        qa[ds] = as_bf16x8(ld16(sb_ + L::Q_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
-        ga[ds] = as_bf16x8(ld16(sb_ + L::G_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
+        qa[ds] = as_bf16x8(ld16(sb_ + L::Q_N + n_lane + ds * 256));
+        ga[ds] = as_bf16x8(ld16(sb_ + L::G_N + n_lane + ds * 256));
       }
 #pragma unroll
       for (int ds = 0; ds < L::NDS; ++ds) {
@@ -580,9 +589,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
     const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
 
-    // Staging: WPT waves per tensor (Q, then dO); lane = 4 consecutive query rows
-    // (quad qa) x 8 features (group fg), quads fastest across lanes.  A tile
-    // index past the sweep maps to row Tq, whose loads return zeros.
+    // Staging: WPT waves per tensor (Q, then dO); lane sidx = 8 fg + qa holds 4
+    // consecutive query rows (quad qa) x 8 features (group fg).  A tile index
+    // past the sweep maps to row Tq, whose loads return zeros.
     const bool stager = wave >= L::SW0;
     const bool is_g = wave >= L::SW0 + L::WPT;
     const int sidx = ((wave - L::SW0) % L::WPT) * 64 + lane;
@@ -591,7 +600,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     // transposed position of the quad: the middle quads of each 16 queries are
     // swapped, matching the query order of a fragment's MFMA k-slots
     const int tpos = 16 * (qa >> 2) + 4 * (((qa & 1) << 1) | ((qa >> 1) & 1));
-    const int n_off = (is_g ? L::G_N : L::Q_N) + ((4 * qa) * L::NSTR + fg * 8) * 2;
+    const int n_off = (is_g ? L::G_N : L::Q_N) + sidx * 16;     // row 4 qa + i, chunk fg: i NB + 16 sidx
     const int t_off = (is_g ? L::GT_OFF : L::QT_OFF) + ((fg * 8) * L::TSTR + tpos) * 2;
     u32x4 stg[4];
     auto gload = [&](int t) {
@@ -606,7 +615,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         char* N = smem + slot2 * L::STAGE + n_off;
         char* T = smem + slot3 * L::T_BYTES + t_off;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st16(N + i * L::NSTR * 2, stg[i]);
+        for (int i = 0; i < 4; ++i) st16(N + i * L::NB, stg[i]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const u32x2 ev = {lo_lo(stg[0][w], stg[1][w]), lo_lo(stg[2][w], stg[3][w])};
