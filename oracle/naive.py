@@ -20,7 +20,10 @@ algorithm:
             What Actually Happens");
             causal: query r sees key l iff l <= r, otherwise S = -inf
             ([ZtF] "The causal mask, and the tiles you never visit"; top-left
-            alignment when Tq != Tk);
+            alignment when Tq != Tk); optional block masks and sliding windows
+            set further scores to -inf ([ZtF] "Dropout, block-sparsity, and
+            other real-kernel details"); a row left without any key has no
+            softmax and is given O = 0, lse = -inf;
             P = softmax(S) row-wise with the row maximum subtracted,
             O = P V ([Atlas] "Standard attention, and why it's wasteful");
             lse_r = m_r + ln sum_l exp(S_rl - m_r), natural log of the scaled
@@ -51,7 +54,7 @@ import numpy as np
 
 __all__ = [
     "scores_head", "probs_head", "forward_head", "backward_head",
-    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK", "dq_rows",
+    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK", "dq_rows", "window_allowed",
 ]
 
 MASK_BLOCK = 128   # side of a block-mask block, in query rows and in keys
@@ -70,6 +73,22 @@ def _visible(Tk: int, rows: np.ndarray, causal: bool) -> np.ndarray | None:
     return np.arange(Tk)[None, :] <= rows[:, None]
 
 
+def window_allowed(Tk: int, rows, window) -> np.ndarray:
+    """Boolean [len(rows), Tk]: key l inside the sliding window (wl, wr) of query r,
+    r - wl <= l <= r + wr, a side of -1 being unbounded.  [ZtF] "Dropout,
+    block-sparsity, and other real-kernel details" lists sliding windows among the
+    masks that are functions of (r, l); (-1, 0) is the causal mask, (-1, -1) none."""
+    wl, wr = window
+    rows = np.asarray(rows)
+    keys = np.arange(Tk)[None, :]
+    ok = np.ones((len(rows), Tk), bool)
+    if wl >= 0:
+        ok &= keys >= rows[:, None] - wl
+    if wr >= 0:
+        ok &= keys <= rows[:, None] + wr
+    return ok
+
+
 def block_allowed(Tq: int, Tk: int, block_mask_h, rows=None) -> np.ndarray:
     """Boolean [len(rows), Tk] from a block mask [ceil(Tq/128)][ceil(Tk/128)] of one head.
 
@@ -81,9 +100,9 @@ def block_allowed(Tq: int, Tk: int, block_mask_h, rows=None) -> np.ndarray:
     return bm[rows // MASK_BLOCK][:, np.arange(Tk) // MASK_BLOCK]
 
 
-def scores_head(q, k, scale, causal, rows=None, block_mask=None):
+def scores_head(q, k, scale, causal, rows=None, block_mask=None, window=None):
     """Scaled, masked scores S[rows, :] = c q k^T with -inf where masked
-    (causal and/or a block mask of this head)."""
+    (causal, a block mask of this head and/or a sliding window (wl, wr))."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
@@ -93,6 +112,8 @@ def scores_head(q, k, scale, causal, rows=None, block_mask=None):
         S = np.where(vis, S, -np.inf)
     if block_mask is not None:
         S = np.where(block_allowed(q.shape[0], k.shape[0], block_mask, rows), S, -np.inf)
+    if window is not None:
+        S = np.where(window_allowed(k.shape[0], rows, window), S, -np.inf)
     return S
 
 
@@ -112,29 +133,29 @@ def _softmax_rows(S):
     return P, lse
 
 
-def probs_head(q, k, scale, causal, rows=None, block_mask=None):
+def probs_head(q, k, scale, causal, rows=None, block_mask=None, window=None):
     """P[rows, :] = softmax(S) and lse[rows] for one head."""
-    return _softmax_rows(scores_head(q, k, scale, causal, rows, block_mask))
+    return _softmax_rows(scores_head(q, k, scale, causal, rows, block_mask, window))
 
 
-def forward_head(q, k, v, scale, causal, rows=None, block_mask=None):
+def forward_head(q, k, v, scale, causal, rows=None, block_mask=None, window=None):
     """O[rows] = softmax(c q k^T) v and lse[rows] for one head.
 
     q [Tq, d], k [Tk, d], v [Tk, dv].  Each output row depends only on its own
     query and all keys, so a subset `rows` is computed exactly by the same
     definition (used where the full T x T matrix would not fit in memory).
     """
-    P, lse = probs_head(q, k, scale, causal, rows, block_mask)
+    P, lse = probs_head(q, k, scale, causal, rows, block_mask, window)
     return P @ np.asarray(v, dtype=np.float64), lse
 
 
-def backward_head(q, k, v, do, scale, causal, block_mask=None):
+def backward_head(q, k, v, do, scale, causal, block_mask=None, window=None):
     """Gradients of sum(O * dO) for one head: returns dQ, dK, dV, O, lse, D."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    P, lse = probs_head(q, k, scale, causal, block_mask=block_mask)
+    P, lse = probs_head(q, k, scale, causal, block_mask=block_mask, window=window)
     O = P @ v
     dV = P.T @ do
     dP = do @ v.T
@@ -145,7 +166,7 @@ def backward_head(q, k, v, do, scale, causal, block_mask=None):
     return dQ, dK, dV, O, lse, D
 
 
-def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None):
+def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None, window=None):
     """dQ[rows] of one head by the same chain rule ([ZtF] "The backward pass,
     derived"): row r of dQ = c dS_r K needs only row r of P, of dP = dO V^T and
     D_r = dO_r . O_r, so sampled rows are exact without the T x T matrices."""
@@ -153,7 +174,7 @@ def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do_r = np.asarray(do, dtype=np.float64)[rows]
-    P, _ = probs_head(q, k, scale, causal, rows, block_mask)
+    P, _ = probs_head(q, k, scale, causal, rows, block_mask, window)
     O = P @ v
     D = np.sum(do_r * O, axis=1)
     dS = P * (do_r @ v.T - D[:, None])
@@ -187,12 +208,13 @@ def _head_mask(block_mask, h):
     return bm[0] if bm.shape[0] == 1 else bm[h]
 
 
-def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_mask=None):
+def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_mask=None, window=None):
     """Batched forward over [B, H, T, d] arrays.
 
     heads: optional list of (b, h) pairs to compute (others are left NaN);
     rows: optional query-row subset applied to every selected head;
-    block_mask: optional uint8 [Hm][ceil(Tq/128)][ceil(Tk/128)], Hm in {1, H}.
+    block_mask: optional uint8 [Hm][ceil(Tq/128)][ceil(Tk/128)], Hm in {1, H};
+    window: optional sliding window (wl, wr), see window_allowed.
     Returns O [B, H, n_rows, d] and lse [B, H, n_rows] in float64.
     """
     B, H, Tq, _ = Q.shape
@@ -204,7 +226,7 @@ def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_m
     def run(bh):
         b, h = bh
         O[b, h], L[b, h] = forward_head(Q[b, h], K[b, h], V[b, h], scale, causal, rows,
-                                        _head_mask(block_mask, h))
+                                        _head_mask(block_mask, h), window)
 
     ex, nw = _pool(workers)
     with _one_blas_thread() if nw > 1 else _nullctx(), ex:
@@ -212,7 +234,7 @@ def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_m
     return O, L
 
 
-def backward(Q, K, V, dO, scale, causal, heads=None, workers=None, block_mask=None):
+def backward(Q, K, V, dO, scale, causal, heads=None, workers=None, block_mask=None, window=None):
     """Batched backward over [B, H, T, d] arrays; returns dQ, dK, dV, O, lse."""
     B, H, Tq, d = Q.shape
     Tk = K.shape[2]
@@ -226,7 +248,7 @@ def backward(Q, K, V, dO, scale, causal, heads=None, workers=None, block_mask=No
     def run(bh):
         b, h = bh
         dQ[b, h], dK[b, h], dV[b, h], O[b, h], L[b, h], _ = backward_head(
-            Q[b, h], K[b, h], V[b, h], dO[b, h], scale, causal, _head_mask(block_mask, h))
+            Q[b, h], K[b, h], V[b, h], dO[b, h], scale, causal, _head_mask(block_mask, h), window)
 
     ex, nw = _pool(workers)
     with _one_blas_thread() if nw > 1 else _nullctx(), ex:
