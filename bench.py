@@ -97,6 +97,16 @@ def mask_pairs(m, Tq: int, Tk: int, causal: bool):
 ORACLE_HEAD_BYTES = 1 << 30                     # largest T x T float64 matrix timed on whole heads
 
 
+def window_pairs(Tq: int, Tk: int, window) -> float:
+    """Visible (query, key) pairs of one head under a sliding window (wl, wr)."""
+    import numpy as np
+    wl, wr = window
+    r = np.arange(Tq, dtype=np.int64)
+    lo = np.maximum(0, r - wl) if wl >= 0 else np.zeros_like(r)
+    hi = np.minimum(Tk - 1, r + wr) if wr >= 0 else np.full_like(r, Tk - 1)
+    return float(np.maximum(0, hi - lo + 1).sum())
+
+
 def cpu_baseline_rows(w, raw, seconds: float, cores: int):
     """For heads too large for the oracle's backward (its T x T matrices): time the
     oracle's forward on sampled query rows, one head per thread."""
@@ -114,16 +124,20 @@ def cpu_baseline_rows(w, raw, seconds: float, cores: int):
         q, k, v = (as_f64(raw[x][bi, hi], w.dtype)[None] for x in ("q", "k", "v"))
         rows = np.sort(rng.choice(w.Tq, size=min(nrows, w.Tq), replace=False))
         t0 = time.perf_counter()
-        naive.forward(q, k, v, scale, w.causal, rows=rows, workers=cores)
+        naive.forward(q, k, v, scale, w.causal, rows=rows, workers=cores, window=w.window)
         t_total += time.perf_counter() - t0
-        pairs = float(np.sum(np.minimum(rows + 1, w.Tk))) if w.causal else float(len(rows)) * w.Tk
+        if w.window is not None:
+            pairs = float(naive.window_allowed(w.Tk, rows, w.window).sum())
+        else:
+            pairs = float(np.sum(np.minimum(rows + 1, w.Tk))) if w.causal else float(len(rows)) * w.Tk
         flops += 4.0 * w.d * pairs * len(batch)
         done += len(batch)
         rounds += 1
         log(f"[cpu_baseline] {rounds} rounds of {len(batch)} heads x {len(rows)} rows in {t_total:.1f} s")
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 NumPy oracle, forward only, {rounds} rounds of {cores} (batch, head) slices x "
-                      f"{nrows} random query rows of the same workload (T={w.Tq}, d={w.d}, causal={w.causal}), "
+                      f"{nrows} random query rows of the same workload (T={w.Tq}, d={w.d}, causal={w.causal}, "
+                      f"window={w.window}), "
                       f"{t_total:.1f} s on {cores} threads with one BLAS thread each; its backward needs whole "
                       f"T x T matrices per head ({w.Tq * w.Tk * 8 / 2**30:.0f} GiB each in float64), so only the "
                       f"forward is timed; FLOPs counted as for the GPU"}
@@ -269,14 +283,18 @@ def main(argv=None):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        if bmask is None:
+        if w.window is not None:
+            fa.fa_fwd_window(q, k, v, o, lse, w.window, stream=stream)
+        elif bmask is None:
             fa.fa_fwd(q, k, v, o, lse, causal=w.causal, stream=stream)
         else:
             fa.fa_fwd_masked(q, k, v, o, lse, bmask, causal=w.causal, stream=stream)
         for i, ph in enumerate(phases):
             if ev is not None:
                 ev[i + 1].record(stream)
-            if bmask is None:
+            if w.window is not None:
+                fa.fa_bwd_window_phases(q, k, v, o, do, lse, dq, dk, dv, w.window, ws, ph, stream=stream)
+            elif bmask is None:
                 fa.fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, ws, ph, causal=w.causal, stream=stream)
             else:
                 fa.fa_bwd_masked_phases(q, k, v, o, do, lse, dq, dk, dv, bmask, ws, ph, causal=w.causal,
@@ -310,6 +328,9 @@ def main(argv=None):
     f_fwd, f_bwd = w.flops_fwd(), w.flops_bwd()
     if bmask_np is not None:                    # kept pairs only: 4 d per visible (query, key) pair
         f_fwd = 4.0 * d * B * float(mask_pairs(bmask_np, Tq, Tk, w.causal).sum())
+        f_bwd = 2.5 * f_fwd
+    if w.window is not None:                    # pairs inside the window only
+        f_fwd = 4.0 * d * B * H * window_pairs(Tq, Tk, w.window)
         f_bwd = 2.5 * f_fwd
     total = f_fwd + f_bwd
     value = total / (ms * 1e-3) / 1e12
@@ -345,6 +366,9 @@ def main(argv=None):
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
+    if w.window is not None:
+        out["config"].update(window=list(w.window),
+                             flops="4 d per (query, key) pair inside the window forward, 2.5 x that backward")
     if bmask_np is not None:
         out["config"].update(block_mask="seeded Bernoulli per 128 x 128 block, one per head, diagonal kept",
                              kept_blocks=round(float(bmask_np.mean()), 4),

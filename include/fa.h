@@ -185,6 +185,36 @@ int fa_bwd_masked_phases(const void* Q, const void* K, const void* V, const void
                          int mask_heads, void* workspace, size_t workspace_bytes, int phases,
                          void* stream);
 
+/*
+ * Sliding-window attention ([ZtF] "Dropout, block-sparsity, and other
+ * real-kernel details": windows are masks that are functions of (r, l)): the
+ * same operation as fa_fwd / fa_bwd with key l visible from query r iff
+ *   r - window_left <= l <= r + window_right,
+ * each side >= 0, or -1 for unbounded (top-left alignment, as for causal).
+ * (-1, 0) is causal attention and (-1, -1) full attention; they run the
+ * corresponding fa_fwd / fa_bwd kernels.  Key blocks wholly outside a query
+ * block's band (and query tiles outside a key block's) are never read or
+ * computed, so work grows with the window, not with Tk.  A query row that
+ * sees no key (possible when Tq > Tk + window_left) gets O = 0 and lse =
+ * -inf, and its dQ is 0.  bfloat16 inputs only.  Other arguments, layouts,
+ * workspace and outputs as fa_fwd / fa_bwd / fa_bwd_phases.  Errors as those,
+ * plus FA_ERR_SHAPE for a side below -1 and FA_ERR_DTYPE for float32 inputs.
+ * Results repeat bit for bit.
+ */
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* lse,
+                  int B, int H, int Tq, int Tk, int d, float scale,
+                  int window_left, int window_right, int dtype, int out_dtype, void* stream);
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* lse, void* dQ, void* dK, void* dV,
+                  int B, int H, int Tq, int Tk, int d, float scale,
+                  int window_left, int window_right, int dtype, int o_dtype, int grad_dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_window_phases(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* lse, void* dQ, void* dK, void* dV,
+                         int B, int H, int Tq, int Tk, int d, float scale,
+                         int window_left, int window_right, int dtype, int o_dtype, int grad_dtype,
+                         void* workspace, size_t workspace_bytes, int phases, void* stream);
+
 /* Static, human-readable text for an fa_status value (never NULL). */
 const char* fa_strerror(int status);
 

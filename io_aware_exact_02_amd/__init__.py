@@ -23,7 +23,8 @@ __all__ = [
     "FA_F32", "FA_BF16", "FA_BWD_PRE", "FA_BWD_MAIN", "FA_BWD_POST", "FA_BWD_ALL", "FAError", "LIB_PATH", "library", "fa_fwd", "fa_bwd",
     "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "forward_splitkv", "fa_fwd_masked", "fa_bwd_masked",
-    "fa_bwd_masked_phases", "forward_masked", "backward_masked", "MASK_BLOCK", "EXPORTED_SYMBOLS",
+    "fa_bwd_masked_phases", "forward_masked", "backward_masked", "MASK_BLOCK", "fa_fwd_window", "fa_bwd_window",
+    "fa_bwd_window_phases", "forward_window", "backward_window", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32 = 0
@@ -31,7 +32,8 @@ FA_BF16 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror",
                     "fa_abi_version", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_masked",
-                    "fa_bwd_masked", "fa_bwd_masked_phases")
+                    "fa_bwd_masked", "fa_bwd_masked_phases", "fa_fwd_window", "fa_bwd_window",
+                    "fa_bwd_window_phases")
 MASK_BLOCK = 128          # block-mask granularity, in query rows and in keys
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST, FA_BWD_ALL = 1, 2, 4, 7
 
@@ -75,6 +77,12 @@ def library() -> ctypes.CDLL:
     lib.fa_bwd_masked.restype = i
     lib.fa_bwd_masked_phases.argtypes = lib.fa_bwd.argtypes[:19] + [vp, i, vp, sz, i, vp]
     lib.fa_bwd_masked_phases.restype = i
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
+    lib.fa_fwd_window.restype = i
+    lib.fa_bwd_window.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_window.restype = i
+    lib.fa_bwd_window_phases.argtypes = lib.fa_bwd_window.argtypes[:-1] + [i, vp]
+    lib.fa_bwd_window_phases.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     _lib = lib
@@ -281,6 +289,66 @@ def fa_bwd_masked_phases(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace,
         raise FAError(st, "fa_bwd_masked_phases")
 
 
+def _window(window):
+    wl, wr = (int(x) for x in window)
+    return wl, wr
+
+
+def fa_fwd_window(q, k, v, o, lse, window, *, scale=None, stream=None) -> None:
+    """Sliding-window forward (bf16 inputs): key l is visible from query r iff
+    r - window[0] <= l <= r + window[1] (-1 = unbounded side)."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    _check(k, "k", (B, H, Tk, d), q.dtype, dev)
+    _check(v, "v", (B, H, Tk, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    wl, wr = _window(window)
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = library().fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 B, H, Tq, Tk, d, c, wl, wr, _dtype_code(q), _dtype_code(o),
+                                 _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_fwd_window")
+
+
+def fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, window, workspace, *, scale=None, stream=None) -> None:
+    """Sliding-window backward (bf16 inputs) into caller-provided dq, dk, dv."""
+    fa_bwd_window_phases(q, k, v, o, do, lse, dq, dk, dv, window, workspace, FA_BWD_ALL, scale=scale,
+                         stream=stream)
+
+
+def fa_bwd_window_phases(q, k, v, o, do, lse, dq, dk, dv, window, workspace, phases, *, scale=None,
+                         stream=None) -> None:
+    """The named phases of the sliding-window backward (an OR of FA_BWD_PRE, _MAIN, _POST)."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    for name, t, T in (("k", k, Tk), ("v", v, Tk), ("do", do, Tq)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    _check(dq, "dq", (B, H, Tq, d), None, dev)
+    _check(dk, "dk", (B, H, Tk, d), dq.dtype, dev)
+    _check(dv, "dv", (B, H, Tk, d), dq.dtype, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    wl, wr = _window(window)
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = library().fa_bwd_window_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk,
+                                        d, c, wl, wr, _dtype_code(q), _dtype_code(o), _dtype_code(dq),
+                                        workspace.data_ptr(), nbytes, int(phases), _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_bwd_window_phases")
+
+
 def forward(q, k, v, *, causal=False, scale=None, out_dtype=None, stream=None):
     """Allocate O and lse with torch and run fa_fwd.  Returns (O, lse).
 
@@ -353,4 +421,31 @@ def backward_masked(q, k, v, o, do, lse, block_mask, *, causal=False, scale=None
         raise ValueError("invalid arguments for fa_bwd_masked")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     fa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, block_mask, ws, scale=scale, causal=causal, stream=stream)
+    return dq, dk, dv
+
+
+def forward_window(q, k, v, window, *, scale=None, out_dtype=None, stream=None):
+    """Allocate O and lse with torch and run fa_fwd_window.  Returns (O, lse)."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    o = torch.empty(q.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    fa_fwd_window(q, k, v, o, lse, window, scale=scale, stream=stream)
+    return o, lse
+
+
+def backward_window(q, k, v, o, do, lse, window, *, scale=None, grad_dtype=None, stream=None):
+    """Allocate gradients and workspace with torch and run fa_bwd_window.  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty((B, H, Tq, d), dtype=gd, device=q.device)
+    dk = torch.empty((B, H, Tk, d), dtype=gd, device=q.device)
+    dv = torch.empty((B, H, Tk, d), dtype=gd, device=q.device)
+    nbytes = fa_bwd_workspace_bytes(B, H, Tq, Tk, d, _dtype_code(q), _dtype_code(dq))
+    if nbytes == 0:
+        raise ValueError("invalid arguments for fa_bwd_window")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, window, ws, scale=scale, stream=stream)
     return dq, dk, dv

@@ -34,10 +34,28 @@ int check_mask(const unsigned char* block_mask, int mask_heads, int H, int dtype
   return FA_OK;
 }
 
+// sliding window (wl, wr): each side >= 0, or -1 for unbounded
+int check_window(int wl, int wr, int dtype) {
+  if (wl < -1 || wr < -1) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  return FA_OK;
+}
+
+// An unbounded window side becomes a bound past any index (sequences are below 2^24).
+int window_side(int w) { return w < 0 ? (1 << 30) : w; }
+
+// The window kernels serve proper windows; (-1, -1) is full attention and (-1, 0)
+// causal, which the dense kernels handle.  Returns 1 if the window kernels apply,
+// and sets causal for the other two.
+int window_mode(int wl, int wr, int* causal) {
+  *causal = (wl < 0 && wr == 0) ? 1 : 0;
+  return !(wl < 0 && (wr < 0 || wr == 0));
+}
+
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
              void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
              int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads, void* workspace,
-             size_t workspace_bytes, int phases, void* stream);
+             size_t workspace_bytes, int phases, void* stream, int win = 0, int wl = 0, int wr = 0);
 
 }  // namespace
 
@@ -112,6 +130,43 @@ int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* l
                              static_cast<hipStream_t>(stream), block_mask, mask_heads);
 }
 
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
+                  int d, float scale, int window_left, int window_right, int dtype, int out_dtype, void* stream) {
+  if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, Tq, Tk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_window(window_left, window_right, dtype);
+  if (st != FA_OK) return st;
+  if (!valid_dtype(out_dtype)) return FA_ERR_DTYPE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse)) return FA_ERR_ALIGN;
+  int causal = 0;
+  const int win = window_mode(window_left, window_right, &causal);
+  return fa::launch_fwd_bf16(Q, K, V, O, lse, B, H, Tq, Tk, d, scale, causal, out_dtype == FA_F32 ? 1 : 0,
+                             static_cast<hipStream_t>(stream), nullptr, 1, win, window_side(window_left),
+                             window_side(window_right));
+}
+
+int fa_bwd_window_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                         const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d,
+                         float scale, int window_left, int window_right, int dtype, int o_dtype, int grad_dtype,
+                         void* workspace, size_t workspace_bytes, int phases, void* stream) {
+  const int st = check_window(window_left, window_right, dtype);
+  if (st != FA_OK) return st;
+  int causal = 0;
+  const int win = window_mode(window_left, window_right, &causal);
+  return bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, dtype, o_dtype, grad_dtype,
+                  nullptr, 1, workspace, workspace_bytes, phases, stream, win, window_side(window_left),
+                  window_side(window_right));
+}
+
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                  void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int window_left,
+                  int window_right, int dtype, int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return fa_bwd_window_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, window_left, window_right,
+                              dtype, o_dtype, grad_dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
 int fa_bwd_masked_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                          const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d,
                          float scale, int causal, int dtype, int o_dtype, int grad_dtype,
@@ -137,7 +192,7 @@ namespace {
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
              void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
              int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads, void* workspace,
-             size_t workspace_bytes, int phases, void* stream) {
+             size_t workspace_bytes, int phases, void* stream, int win, int wl, int wr) {
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return FA_ERR_NULL;
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -159,7 +214,7 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
   if (dtype == FA_BF16)
     return fa::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal,
                                o_dtype == FA_F32 ? 1 : 0, grad_dtype == FA_F32 ? 1 : 0, workspace, phases, s,
-                               block_mask, mask_heads);
+                               block_mask, mask_heads, win, wl, wr);
   return fa::launch_bwd_f32(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, workspace, phases, s);
 }
 

@@ -46,10 +46,11 @@ static_assert(kBKC == kMaskBlock, "one key-block workgroup per mask column");
 // all tiles from it0 on, or (masked) those whose 128-query block keeps this key
 // block.  count() is their number, next(t) the first visible tile >= t (nqt
 // when none is left).  Every lane of the wave must be active in both.
-template <bool MASKED>
+template <bool MASKED, bool WIN = false>
 struct KeyBlockTiles {
   const uint8_t* mcol;     // mask column of this key block (stride nmk), MASKED only
   int nmk, nmq, nvw, nqt, it0, lane;
+  int nqe = 0;             // WIN: one past the last query tile the window lets see the block
   int cw = -1;             // the word last read is kept in scalar registers
   unsigned long long cbits = 0;
 
@@ -76,6 +77,7 @@ struct KeyBlockTiles {
     return w * 64 + (int)__builtin_ctzll(bits);
   }
   __device__ int next(int t) {
+    if constexpr (WIN) return t < nqe ? t : nqt;
     if constexpr (MASKED) {
       if (t >= nqt) return nqt;
       if (row(t / kTilesPerMaskRow)) return t;
@@ -99,6 +101,8 @@ struct KeyBlockTiles {
       if (row(rlo)) n -= it0 - rlo * kTilesPerMaskRow;           // the first block starts at it0
       if (row(nmq - 1)) n -= nmq * kTilesPerMaskRow - nqt;       // the last block is ragged
       return n;
+    } else if constexpr (WIN) {
+      return max(0, nqe - it0);
     } else {
       return nqt - it0;
     }
@@ -144,14 +148,14 @@ struct W4Layout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL, bool MASKED>
+template <int D, bool CAUSAL, bool MASKED, bool WIN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                       const float* __restrict__ Ln, const float* __restrict__ Dn,
                       void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e,
                       int nkb, int grad_f32, const uint8_t* __restrict__ bmask, int H, long long mask_hstride,
-                      int nmk) {
+                      int nmk, int wl, int wr) {
   using L = W4Layout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
@@ -193,8 +197,9 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     }
 
   const int nqt = (Tq + kBQ - 1) / kBQ;
-  const int it0 = CAUSAL ? min(k0 / kBQ, nqt) : 0;
-  KeyBlockTiles<MASKED> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  const int it0 = WIN ? min(max(0, k0 - wr) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
+  KeyBlockTiles<MASKED, WIN> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  if constexpr (WIN) tiles.nqe = min(nqt, (min(k0 + kBKC, Tk) - 1 + wl) / kBQ + 1);
   const int n = tiles.count();                  // query tiles in the sweep
 
   // ---- staging of one query tile (Q_i, dO_i, Ln_i, Dn_i) ----
@@ -299,6 +304,13 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
+    }
+    if (WIN && !(kw0 >= r0 + kBQ - 1 - wl && kw0 + kKeysPerWave - 1 <= r0 + wr)) {   // crosses a band edge
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = r0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (mykey < qr - wl || mykey > qr + wr) p[r] = 0.f;
+      }
     }
     bf16x8 pb[2], sbf[2];
 #pragma unroll
@@ -459,12 +471,12 @@ struct KvLayout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL, bool MASKED>
+template <int D, bool CAUSAL, bool MASKED, bool WIN>
 __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
     void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e, int nkb, int grad_f32,
-    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk) {
+    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr) {
   using L = KvLayout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
@@ -482,12 +494,13 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   const int mykey = kw0 + l32;
 
   const int nqt = (Tq + kBQ - 1) / kBQ;
-  const int it0 = CAUSAL ? min(k0 / kBQ, nqt) : 0;
+  const int it0 = WIN ? min(max(0, k0 - wr) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
   // tile t covers query rows t kBQ ..; a tile past the sweep reads row Tq (zeros)
   auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
 
   // visible query tiles: all from it0 on, or (masked) those whose block keeps this key block
-  KeyBlockTiles<MASKED> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  KeyBlockTiles<MASKED, WIN> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  if constexpr (WIN) tiles.nqe = min(nqt, (min(k0 + kBKC, Tk) - 1 + wl) / kBQ + 1);
   const int n = tiles.count();                  // query tiles in the sweep
   auto next_tile = [&](int t) { return tiles.next(t); };
 
@@ -557,6 +570,13 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
+      }
+      if (WIN && !(kw0 >= r0 + kBQ - 1 - wl && kw0 + kKeysPerWave - 1 <= r0 + wr)) {   // crosses a band edge
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qr = r0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (mykey < qr - wl || mykey > qr + wr) p[r] = 0.f;
+        }
       }
       // fragments for the gradient wave: [P^T t=0, P^T t=1, dS^T t=0, dS^T t=1], 1 KiB each
       char* fb = smem + L::F_OFF + ST * L::F_BYTES + wq * L::F_WAVE + lane * 16;
@@ -777,13 +797,13 @@ __device__ __forceinline__ int dq_swz(int r) { return NC >= 16 ? (r & 15) : ((r 
 // rows.  Both rows go into LDS bitmaps (bit c = key block c visible); the
 // workgroup visits the key tiles that either row can see, and a wave computes
 // only those its own row can see.
-template <int D, bool CAUSAL, bool MASKED>
+template <int D, bool CAUSAL, bool MASKED, bool WIN>
 __global__ __launch_bounds__(DqLayout<D>::THREADS)
 __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
     void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32,
-    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk) {
+    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr) {
   using L = DqLayout<D>;
   constexpr int BC = L::BC;
   static_assert(kMaskBlock % BC == 0 && L::BR % kMaskBlock == 0 && L::BR <= 2 * kMaskBlock,
@@ -826,6 +846,11 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 
   int ntile = (Tk + BC - 1) / BC;
   if (CAUSAL) ntile = min(ntile, (min(q0 + L::BR, Tq) - 1) / BC + 1);
+  int jfirst = 0;                                     // first key block any row of the block can see
+  if constexpr (WIN) {
+    ntile = min(ntile, (min(q0 + L::BR, Tq) - 1 + wr) / BC + 1);
+    jfirst = max(0, q0 - wl) / BC;
+  }
 
   // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled
   const rsrc_t rkv = wave < L::WAVES / 2 ? rk : rv;
@@ -920,7 +945,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   };
 
   auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
-  const int j0 = next_tile(0);
+  const int j0 = next_tile(jfirst);
   kv_dma(first_row(j0), 0);
   t_load(first_row(j0));
   t_store(0);
@@ -935,8 +960,10 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     t_load(first_row(jn));
     kv_dma(first_row(jn), ST ^ 1);
     const int kt0 = j * BC;
-    if ((!CAUSAL || kt0 <= qw + 31) && sees) {          // some key of the block is visible to this wave
-      const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk);
+    const bool in_band = !WIN || (kt0 <= qw + 31 + wr && kt0 + BC - 1 >= qw - wl);
+    if ((!CAUSAL || kt0 <= qw + 31) && sees && in_band) {   // some key of the block is visible to this wave
+      const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk) ||
+                        (WIN && !(kt0 >= qw + 31 - wl && kt0 + BC - 1 <= qw + wr));
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb) {
         // S^T and dP^T - D for 32 keys: register r = key kt0 + 32 kb + 8(r/4)+4hf+r%4, lane = query
@@ -963,7 +990,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= Tk || (CAUSAL && key > myq)) p[r] = 0.f;
+            if (key >= Tk || (CAUSAL && key > myq) || (WIN && (key < myq - wl || key > myq + wr))) p[r] = 0.f;
           }
         }
         bf16x8 sf[2];
@@ -1018,7 +1045,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
       j = jn;
     }
   } else {
-    for (int j = 0; j < ntile; j += 2) {
+    for (int j = j0; j < ntile; j += 2) {
       step(j, j + 1, 0);
       if (j + 1 < ntile) step(j + 1, j + 2, 1);
     }
@@ -1046,7 +1073,8 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 template <int D>
 int bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
         void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int o_f32, int grad_f32,
-        void* workspace, int phases, hipStream_t stream, const uint8_t* bmask, int mask_heads) {
+        void* workspace, int phases, hipStream_t stream, const uint8_t* bmask, int mask_heads, int win, int wl,
+        int wr) {
   using LQ = DqLayout<D>;
   const long long rows = (long long)B * H * Tq;
   const int nkb = (Tk + kBKC - 1) / kBKC;
@@ -1080,37 +1108,40 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
     constexpr int KV_THREADS = D == 256 ? 256 : 512;
     auto kv = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)nblk), dim3(KV_THREADS), 0, stream, q, k, v, g, Ln, Dn, dK, dV, Tq,
-                         Tk, scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk);
+                         Tk, scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk, wl, wr);
     };
     if constexpr (D == 256) {
-      if (bmask) {
-        if (causal) kv(bwd_kv_w4_kernel<D, true, true>);
-        else kv(bwd_kv_w4_kernel<D, false, true>);
+      if (win) kv(bwd_kv_w4_kernel<D, false, false, true>);
+      else if (bmask) {
+        if (causal) kv(bwd_kv_w4_kernel<D, true, true, false>);
+        else kv(bwd_kv_w4_kernel<D, false, true, false>);
       } else {
-        if (causal) kv(bwd_kv_w4_kernel<D, true, false>);
-        else kv(bwd_kv_w4_kernel<D, false, false>);
+        if (causal) kv(bwd_kv_w4_kernel<D, true, false, false>);
+        else kv(bwd_kv_w4_kernel<D, false, false, false>);
       }
     } else {
-      if (bmask) {
-        if (causal) kv(bwd_kv_kernel<D, true, true>);
-        else kv(bwd_kv_kernel<D, false, true>);
+      if (win) kv(bwd_kv_kernel<D, false, false, true>);
+      else if (bmask) {
+        if (causal) kv(bwd_kv_kernel<D, true, true, false>);
+        else kv(bwd_kv_kernel<D, false, true, false>);
       } else {
-        if (causal) kv(bwd_kv_kernel<D, true, false>);
-        else kv(bwd_kv_kernel<D, false, false>);
+        if (causal) kv(bwd_kv_kernel<D, true, false, false>);
+        else kv(bwd_kv_kernel<D, false, false, false>);
       }
     }
   }
   if (phases & FA_BWD_POST) {
     auto dqk = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)nqblk), dim3(LQ::THREADS), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq,
-                         Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk);
+                         Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr);
     };
-    if (bmask) {
-      if (causal) dqk(bwd_dq_kernel<D, true, true>);
-      else dqk(bwd_dq_kernel<D, false, true>);
+    if (win) dqk(bwd_dq_kernel<D, false, false, true>);
+    else if (bmask) {
+      if (causal) dqk(bwd_dq_kernel<D, true, true, false>);
+      else dqk(bwd_dq_kernel<D, false, true, false>);
     } else {
-      if (causal) dqk(bwd_dq_kernel<D, true, false>);
-      else dqk(bwd_dq_kernel<D, false, false>);
+      if (causal) dqk(bwd_dq_kernel<D, true, false, false>);
+      else dqk(bwd_dq_kernel<D, false, false, false>);
     }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -1121,11 +1152,11 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                     int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream, const uint8_t* bmask,
-                    int mask_heads) {
+                    int mask_heads, int win, int wl, int wr) {
   switch (d) {
-    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads);
-    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads);
-    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads);
+    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, win, wl, wr);
+    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, win, wl, wr);
+    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, win, wl, wr);
     default: return FA_ERR_HEADDIM;
   }
 }

@@ -55,6 +55,7 @@ class Workload:
     qk_spread: float = 1.0
     seed: int = BASE_SEED
     mask_density: float | None = None   # block-sparse: fraction of kept 128 x 128 blocks (one mask per head)
+    window: tuple | None = None         # sliding window (wl, wr): keys r - wl .. r + wr of query r
 
     def flops_fwd(self) -> float:
         """4 B H Tq Tk d, halved when causal (square causal: visible pairs ~ T^2 / 2)."""
@@ -82,6 +83,9 @@ WORKLOADS = {
     "blocksparse_bf16_b8h32_t4096_d128_s25": Workload("blocksparse_bf16_b8h32_t4096_d128_s25", 8, 32, 4096, 4096,
                                                       128, "bf16", False, True, seed=BASE_SEED + 7,
                                                       mask_density=0.25),
+    # sliding window: 4096 keys up to and including the query's own (window (4095, 0))
+    "swa_bf16_b1h32_t32768_d128_w4096": Workload("swa_bf16_b1h32_t32768_d128_w4096", 1, 32, 32768, 32768, 128,
+                                                 "bf16", False, True, seed=BASE_SEED + 8, window=(4095, 0)),
     # decoding: one query row per head against a long key cache (split-key forward)
     "decode_bf16_b8h16_tq1_tk32768_d128": Workload("decode_bf16_b8h16_tq1_tk32768_d128", 8, 16, 1, 32768, 128,
                                                    "bf16", False, False, seed=BASE_SEED + 6),

@@ -208,3 +208,27 @@ def test_masked_phase_mask(lib):
     bad = list(args)
     bad[19] = None
     assert lib.fa_bwd_masked_phases(*bad, 0, None) == NULL
+
+
+def test_window_argument_errors(lib):
+    def fwd(wl=4, wr=2, dtype=fa.FA_BF16, odtype=fa.FA_BF16, d=128, null_at=None):
+        ptrs = [P] * 5
+        if null_at is not None:
+            ptrs[null_at] = None
+        return lib.fa_fwd_window(*ptrs, 1, 2, 300, 300, d, 0.125, wl, wr, dtype, odtype, None)
+
+    def bwd(wl=4, wr=2, dtype=fa.FA_BF16, ws=P, ws_bytes=1 << 30, phases=None):
+        args = [P] * 9 + [1, 2, 300, 300, 128, 0.125, wl, wr, dtype, dtype, dtype, ws, ws_bytes]
+        if phases is None:
+            return lib.fa_bwd_window(*args, None)
+        return lib.fa_bwd_window_phases(*args, phases, None)
+
+    for i in range(5):
+        assert fwd(null_at=i) == NULL
+    for wl, wr in ((-2, 0), (0, -2), (-5, -5)):
+        assert fwd(wl, wr) == SHAPE and bwd(wl, wr) == SHAPE
+    assert fwd(dtype=fa.FA_F32, odtype=fa.FA_F32) == DTYPE and bwd(dtype=fa.FA_F32) == DTYPE
+    assert fwd(d=96) == HEADDIM
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(phases=8) == PHASE
+    assert bwd(phases=0) == OK              # checks only, launches nothing
