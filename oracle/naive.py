@@ -54,7 +54,7 @@ import numpy as np
 
 __all__ = [
     "scores_head", "probs_head", "forward_head", "backward_head",
-    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK", "dq_rows", "window_allowed",
+    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK", "dq_rows", "window_allowed", "doc_allowed",
 ]
 
 MASK_BLOCK = 128   # side of a block-mask block, in query rows and in keys
@@ -89,6 +89,19 @@ def window_allowed(Tk: int, rows, window) -> np.ndarray:
     return ok
 
 
+def doc_allowed(Tk: int, rows, cu_seqlens) -> np.ndarray:
+    """Boolean [len(rows), Tk]: query r and key l lie in the same document of a packed
+    sequence whose documents start at cu_seqlens[i] and end before cu_seqlens[i + 1]
+    (cu_seqlens[0] = 0, last = sequence length).  [ZtF] "Dropout, block-sparsity, and
+    other real-kernel details" names document masks among the masks that are
+    functions of (r, l); combined with causal, each document is attended causally."""
+    cu = np.asarray(cu_seqlens)
+    rows = np.asarray(rows)
+    doc_r = np.searchsorted(cu, rows, side="right") - 1
+    doc_l = np.searchsorted(cu, np.arange(Tk), side="right") - 1
+    return doc_r[:, None] == doc_l[None, :]
+
+
 def block_allowed(Tq: int, Tk: int, block_mask_h, rows=None) -> np.ndarray:
     """Boolean [len(rows), Tk] from a block mask [ceil(Tq/128)][ceil(Tk/128)] of one head.
 
@@ -100,9 +113,9 @@ def block_allowed(Tq: int, Tk: int, block_mask_h, rows=None) -> np.ndarray:
     return bm[rows // MASK_BLOCK][:, np.arange(Tk) // MASK_BLOCK]
 
 
-def scores_head(q, k, scale, causal, rows=None, block_mask=None, window=None):
-    """Scaled, masked scores S[rows, :] = c q k^T with -inf where masked
-    (causal, a block mask of this head and/or a sliding window (wl, wr))."""
+def scores_head(q, k, scale, causal, rows=None, block_mask=None, window=None, docs=None):
+    """Scaled, masked scores S[rows, :] = c q k^T with -inf where masked (causal, a
+    block mask of this head, a sliding window (wl, wr) and/or documents cu_seqlens)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
@@ -114,6 +127,8 @@ def scores_head(q, k, scale, causal, rows=None, block_mask=None, window=None):
         S = np.where(block_allowed(q.shape[0], k.shape[0], block_mask, rows), S, -np.inf)
     if window is not None:
         S = np.where(window_allowed(k.shape[0], rows, window), S, -np.inf)
+    if docs is not None:
+        S = np.where(doc_allowed(k.shape[0], rows, docs), S, -np.inf)
     return S
 
 
@@ -133,29 +148,29 @@ def _softmax_rows(S):
     return P, lse
 
 
-def probs_head(q, k, scale, causal, rows=None, block_mask=None, window=None):
+def probs_head(q, k, scale, causal, rows=None, block_mask=None, window=None, docs=None):
     """P[rows, :] = softmax(S) and lse[rows] for one head."""
-    return _softmax_rows(scores_head(q, k, scale, causal, rows, block_mask, window))
+    return _softmax_rows(scores_head(q, k, scale, causal, rows, block_mask, window, docs))
 
 
-def forward_head(q, k, v, scale, causal, rows=None, block_mask=None, window=None):
+def forward_head(q, k, v, scale, causal, rows=None, block_mask=None, window=None, docs=None):
     """O[rows] = softmax(c q k^T) v and lse[rows] for one head.
 
     q [Tq, d], k [Tk, d], v [Tk, dv].  Each output row depends only on its own
     query and all keys, so a subset `rows` is computed exactly by the same
     definition (used where the full T x T matrix would not fit in memory).
     """
-    P, lse = probs_head(q, k, scale, causal, rows, block_mask, window)
+    P, lse = probs_head(q, k, scale, causal, rows, block_mask, window, docs)
     return P @ np.asarray(v, dtype=np.float64), lse
 
 
-def backward_head(q, k, v, do, scale, causal, block_mask=None, window=None):
+def backward_head(q, k, v, do, scale, causal, block_mask=None, window=None, docs=None):
     """Gradients of sum(O * dO) for one head: returns dQ, dK, dV, O, lse, D."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    P, lse = probs_head(q, k, scale, causal, block_mask=block_mask, window=window)
+    P, lse = probs_head(q, k, scale, causal, block_mask=block_mask, window=window, docs=docs)
     O = P @ v
     dV = P.T @ do
     dP = do @ v.T
@@ -166,7 +181,7 @@ def backward_head(q, k, v, do, scale, causal, block_mask=None, window=None):
     return dQ, dK, dV, O, lse, D
 
 
-def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None, window=None):
+def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None, window=None, docs=None):
     """dQ[rows] of one head by the same chain rule ([ZtF] "The backward pass,
     derived"): row r of dQ = c dS_r K needs only row r of P, of dP = dO V^T and
     D_r = dO_r . O_r, so sampled rows are exact without the T x T matrices."""
@@ -174,7 +189,7 @@ def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None, window=None):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do_r = np.asarray(do, dtype=np.float64)[rows]
-    P, _ = probs_head(q, k, scale, causal, rows, block_mask, window)
+    P, _ = probs_head(q, k, scale, causal, rows, block_mask, window, docs)
     O = P @ v
     D = np.sum(do_r * O, axis=1)
     dS = P * (do_r @ v.T - D[:, None])
@@ -208,13 +223,15 @@ def _head_mask(block_mask, h):
     return bm[0] if bm.shape[0] == 1 else bm[h]
 
 
-def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_mask=None, window=None):
+def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_mask=None, window=None,
+            docs=None):
     """Batched forward over [B, H, T, d] arrays.
 
     heads: optional list of (b, h) pairs to compute (others are left NaN);
     rows: optional query-row subset applied to every selected head;
     block_mask: optional uint8 [Hm][ceil(Tq/128)][ceil(Tk/128)], Hm in {1, H};
-    window: optional sliding window (wl, wr), see window_allowed.
+    window: optional sliding window (wl, wr), see window_allowed;
+    docs: optional document offsets cu_seqlens, see doc_allowed.
     Returns O [B, H, n_rows, d] and lse [B, H, n_rows] in float64.
     """
     B, H, Tq, _ = Q.shape
@@ -226,7 +243,7 @@ def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_m
     def run(bh):
         b, h = bh
         O[b, h], L[b, h] = forward_head(Q[b, h], K[b, h], V[b, h], scale, causal, rows,
-                                        _head_mask(block_mask, h), window)
+                                        _head_mask(block_mask, h), window, docs)
 
     ex, nw = _pool(workers)
     with _one_blas_thread() if nw > 1 else _nullctx(), ex:
@@ -234,7 +251,7 @@ def forward(Q, K, V, scale, causal, heads=None, rows=None, workers=None, block_m
     return O, L
 
 
-def backward(Q, K, V, dO, scale, causal, heads=None, workers=None, block_mask=None, window=None):
+def backward(Q, K, V, dO, scale, causal, heads=None, workers=None, block_mask=None, window=None, docs=None):
     """Batched backward over [B, H, T, d] arrays; returns dQ, dK, dV, O, lse."""
     B, H, Tq, d = Q.shape
     Tk = K.shape[2]
@@ -248,7 +265,7 @@ def backward(Q, K, V, dO, scale, causal, heads=None, workers=None, block_mask=No
     def run(bh):
         b, h = bh
         dQ[b, h], dK[b, h], dV[b, h], O[b, h], L[b, h], _ = backward_head(
-            Q[b, h], K[b, h], V[b, h], dO[b, h], scale, causal, _head_mask(block_mask, h), window)
+            Q[b, h], K[b, h], V[b, h], dO[b, h], scale, causal, _head_mask(block_mask, h), window, docs)
 
     ex, nw = _pool(workers)
     with _one_blas_thread() if nw > 1 else _nullctx(), ex:
