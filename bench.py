@@ -107,7 +107,18 @@ def window_pairs(Tq: int, Tk: int, window) -> float:
     return float(np.maximum(0, hi - lo + 1).sum())
 
 
-def cpu_baseline_rows(w, raw, seconds: float, cores: int):
+def doc_pairs(cu, causal: bool, rows=None) -> float:
+    """Visible (query, key) pairs of one head under document offsets cu (of the listed
+    query rows only, when given): a row sees its document, up to itself when causal."""
+    import numpy as np
+    cu = np.asarray(cu, np.int64)
+    r = np.arange(int(cu[-1])) if rows is None else np.asarray(rows, np.int64)
+    doc = np.searchsorted(cu, r, side="right") - 1
+    start, end = cu[doc], cu[doc + 1]
+    return float(((r - start + 1) if causal else (end - start)).sum())
+
+
+def cpu_baseline_rows(w, raw, seconds: float, cores: int, docs=None):
     """For heads too large for the oracle's backward (its T x T matrices): time the
     oracle's forward on sampled query rows, one head per thread."""
     import numpy as np
@@ -124,9 +135,11 @@ def cpu_baseline_rows(w, raw, seconds: float, cores: int):
         q, k, v = (as_f64(raw[x][bi, hi], w.dtype)[None] for x in ("q", "k", "v"))
         rows = np.sort(rng.choice(w.Tq, size=min(nrows, w.Tq), replace=False))
         t0 = time.perf_counter()
-        naive.forward(q, k, v, scale, w.causal, rows=rows, workers=cores, window=w.window)
+        naive.forward(q, k, v, scale, w.causal, rows=rows, workers=cores, window=w.window, docs=docs)
         t_total += time.perf_counter() - t0
-        if w.window is not None:
+        if docs is not None:
+            pairs = doc_pairs(docs, w.causal, rows)
+        elif w.window is not None:
             pairs = float(naive.window_allowed(w.Tk, rows, w.window).sum())
         else:
             pairs = float(np.sum(np.minimum(rows + 1, w.Tk))) if w.causal else float(len(rows)) * w.Tk
@@ -137,20 +150,20 @@ def cpu_baseline_rows(w, raw, seconds: float, cores: int):
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 NumPy oracle, forward only, {rounds} rounds of {cores} (batch, head) slices x "
                       f"{nrows} random query rows of the same workload (T={w.Tq}, d={w.d}, causal={w.causal}, "
-                      f"window={w.window}), "
+                      f"window={w.window}{', packed documents' if docs is not None else ''}), "
                       f"{t_total:.1f} s on {cores} threads with one BLAS thread each; its backward needs whole "
                       f"T x T matrices per head ({w.Tq * w.Tk * 8 / 2**30:.0f} GiB each in float64), so only the "
                       f"forward is timed; FLOPs counted as for the GPU"}
 
 
-def cpu_baseline(w, raw, seconds: float, bmask=None):
+def cpu_baseline(w, raw, seconds: float, bmask=None, docs=None):
     """Time the float64 oracle's forward+backward on whole heads of the workload
     (with the workload's block mask when it has one)."""
     from oracle import naive
     from io_aware_exact_02_amd.inputs import as_f64
     cores = max(1, min(CPU_SHARE, os.cpu_count() or 1))
     if w.Tq * w.Tk * 8 > ORACLE_HEAD_BYTES and bmask is None:
-        return cpu_baseline_rows(w, raw, seconds, cores)
+        return cpu_baseline_rows(w, raw, seconds, cores, docs)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     scale = 1.0 / math.sqrt(w.d)
     pairs = mask_pairs(bmask, w.Tq, w.Tk, w.causal) if bmask is not None else None
@@ -247,7 +260,7 @@ def main(argv=None):
         return 2
     import torch
     import io_aware_exact_02_amd as fa
-    from io_aware_exact_02_amd.inputs import WORKLOADS, draw_workload, workload_mask
+    from io_aware_exact_02_amd.inputs import WORKLOADS, draw_workload, workload_docs, workload_mask
 
     w = WORKLOADS[a.workload]
     if w.Tq <= 32 and w.dtype == "bf16" and not w.backward:
@@ -279,11 +292,17 @@ def main(argv=None):
     if w.mask_density is not None:
         bmask_np = workload_mask(w, a.density)
         bmask = torch.from_numpy(bmask_np).to(dev)
+    cu_np = cu = None
+    if w.doc_len is not None:
+        cu_np = workload_docs(w)
+        cu = torch.from_numpy(cu_np).to(dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        if w.window is not None:
+        if cu is not None:
+            fa.fa_fwd_docs(q, k, v, o, lse, cu, causal=w.causal, stream=stream)
+        elif w.window is not None:
             fa.fa_fwd_window(q, k, v, o, lse, w.window, stream=stream)
         elif bmask is None:
             fa.fa_fwd(q, k, v, o, lse, causal=w.causal, stream=stream)
@@ -292,7 +311,9 @@ def main(argv=None):
         for i, ph in enumerate(phases):
             if ev is not None:
                 ev[i + 1].record(stream)
-            if w.window is not None:
+            if cu is not None:
+                fa.fa_bwd_docs_phases(q, k, v, o, do, lse, dq, dk, dv, cu, ws, ph, causal=w.causal, stream=stream)
+            elif w.window is not None:
                 fa.fa_bwd_window_phases(q, k, v, o, do, lse, dq, dk, dv, w.window, ws, ph, stream=stream)
             elif bmask is None:
                 fa.fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, ws, ph, causal=w.causal, stream=stream)
@@ -332,6 +353,9 @@ def main(argv=None):
     if w.window is not None:                    # pairs inside the window only
         f_fwd = 4.0 * d * B * H * window_pairs(Tq, Tk, w.window)
         f_bwd = 2.5 * f_fwd
+    if cu_np is not None:                       # pairs inside each document only
+        f_fwd = 4.0 * d * B * H * doc_pairs(cu_np, w.causal)
+        f_bwd = 2.5 * f_fwd
     total = f_fwd + f_bwd
     value = total / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -355,7 +379,7 @@ def main(argv=None):
     cpu = None
     if a.cpu_seconds > 0:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(w, raw, a.cpu_seconds, bmask_np)
+        cpu = cpu_baseline(w, raw, a.cpu_seconds, bmask_np, cu_np)
     out = {
         "metric": METRIC if w.name == DEFAULT_WORKLOAD else f"attention fwd+bwd TFLOP/s ({w.name})",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -369,6 +393,10 @@ def main(argv=None):
     if w.window is not None:
         out["config"].update(window=list(w.window),
                              flops="4 d per (query, key) pair inside the window forward, 2.5 x that backward")
+    if cu_np is not None:
+        out["config"].update(documents=len(cu_np) - 1, doc_len=list(w.doc_len),
+                             doc_offsets="seeded, lengths log-uniform in doc_len, laid end to end",
+                             flops="4 d per (query, key) pair inside a document forward, 2.5 x that backward")
     if bmask_np is not None:
         out["config"].update(block_mask="seeded Bernoulli per 128 x 128 block, one per head, diagonal kept",
                              kept_blocks=round(float(bmask_np.mean()), 4),

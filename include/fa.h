@@ -215,6 +215,42 @@ int fa_bwd_window_phases(const void* Q, const void* K, const void* V, const void
                          int window_left, int window_right, int dtype, int o_dtype, int grad_dtype,
                          void* workspace, size_t workspace_bytes, int phases, void* stream);
 
+/*
+ * Document masks for packed sequences ([ZtF] "Dropout, block-sparsity, and
+ * other real-kernel details": document masks are masks that are functions of
+ * (r, l)): each of the B x H sequences of length T holds ndocs documents laid
+ * end to end, and query r sees key l iff both lie in the same document (and,
+ * when causal != 0, l <= r), i.e. attention runs on every document on its own.
+ *   cu_seqlens  device buffer of int32 [ndocs + 1], 4-byte aligned: document i
+ *               holds positions cu_seqlens[i] .. cu_seqlens[i+1] - 1, with
+ *               cu_seqlens[0] = 0, non-decreasing, cu_seqlens[ndocs] = T
+ *               (empty documents allowed).  One set of offsets serves every
+ *               batch entry and head.  Owned by the caller, read only.
+ *   ndocs       number of documents, >= 1
+ * The library reads the offsets only on the device and cannot check them: with
+ * offsets that break the rules above results are unspecified, but every memory
+ * access stays inside the buffers.  Key blocks outside a query block's
+ * documents (and query tiles outside a key block's) are never read or computed,
+ * so work grows with the document lengths, not with T.  bfloat16 inputs only.
+ * Other arguments (Tq = Tk = T), layouts, workspace and outputs as fa_fwd /
+ * fa_bwd / fa_bwd_phases.  Errors as those, plus FA_ERR_NULL for a missing
+ * cu_seqlens, FA_ERR_SHAPE for ndocs < 1, FA_ERR_ALIGN for a misaligned
+ * cu_seqlens and FA_ERR_DTYPE for float32 inputs.  Results repeat bit for bit.
+ */
+int fa_fwd_docs(const void* Q, const void* K, const void* V, void* O, float* lse,
+                int B, int H, int T, int d, float scale, int causal,
+                const int* cu_seqlens, int ndocs, int dtype, int out_dtype, void* stream);
+int fa_bwd_docs(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* lse, void* dQ, void* dK, void* dV,
+                int B, int H, int T, int d, float scale, int causal,
+                const int* cu_seqlens, int ndocs, int dtype, int o_dtype, int grad_dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_docs_phases(const void* Q, const void* K, const void* V, const void* O,
+                       const void* dO, const float* lse, void* dQ, void* dK, void* dV,
+                       int B, int H, int T, int d, float scale, int causal,
+                       const int* cu_seqlens, int ndocs, int dtype, int o_dtype, int grad_dtype,
+                       void* workspace, size_t workspace_bytes, int phases, void* stream);
+
 /* Static, human-readable text for an fa_status value (never NULL). */
 const char* fa_strerror(int status);
 

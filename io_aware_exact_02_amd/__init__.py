@@ -24,7 +24,8 @@ __all__ = [
     "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror", "fa_abi_version", "forward", "backward",
     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "forward_splitkv", "fa_fwd_masked", "fa_bwd_masked",
     "fa_bwd_masked_phases", "forward_masked", "backward_masked", "MASK_BLOCK", "fa_fwd_window", "fa_bwd_window",
-    "fa_bwd_window_phases", "forward_window", "backward_window", "EXPORTED_SYMBOLS",
+    "fa_bwd_window_phases", "forward_window", "backward_window", "fa_fwd_docs", "fa_bwd_docs",
+    "fa_bwd_docs_phases", "forward_docs", "backward_docs", "EXPORTED_SYMBOLS",
 ]
 
 FA_F32 = 0
@@ -33,7 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror",
                     "fa_abi_version", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_masked",
                     "fa_bwd_masked", "fa_bwd_masked_phases", "fa_fwd_window", "fa_bwd_window",
-                    "fa_bwd_window_phases")
+                    "fa_bwd_window_phases", "fa_fwd_docs", "fa_bwd_docs", "fa_bwd_docs_phases")
 MASK_BLOCK = 128          # block-mask granularity, in query rows and in keys
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST, FA_BWD_ALL = 1, 2, 4, 7
 
@@ -83,6 +84,12 @@ def library() -> ctypes.CDLL:
     lib.fa_bwd_window.restype = i
     lib.fa_bwd_window_phases.argtypes = lib.fa_bwd_window.argtypes[:-1] + [i, vp]
     lib.fa_bwd_window_phases.restype = i
+    lib.fa_fwd_docs.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, i, i, vp]
+    lib.fa_fwd_docs.restype = i
+    lib.fa_bwd_docs.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_docs.restype = i
+    lib.fa_bwd_docs_phases.argtypes = lib.fa_bwd_docs.argtypes[:-1] + [i, vp]
+    lib.fa_bwd_docs_phases.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     _lib = lib
@@ -349,6 +356,69 @@ def fa_bwd_window_phases(q, k, v, o, do, lse, dq, dk, dv, window, workspace, pha
         raise FAError(st, "fa_bwd_window_phases")
 
 
+def _check_docs(cu_seqlens, dev):
+    torch = _torch()
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError(f"cu_seqlens: expected shape (ndocs + 1,) with ndocs >= 1, got {tuple(cu_seqlens.shape)}")
+    _check(cu_seqlens, "cu_seqlens", tuple(cu_seqlens.shape), torch.int32, dev)
+    return int(cu_seqlens.numel()) - 1
+
+
+def fa_fwd_docs(q, k, v, o, lse, cu_seqlens, *, scale=None, causal=False, stream=None) -> None:
+    """Document-masked forward (bf16 inputs) of packed sequences [B, H, T, d]: query r
+    sees key l iff both lie in one document (and l <= r when causal).  `cu_seqlens`:
+    int32 GPU tensor [ndocs + 1] of offsets, 0 first and T last, shared by all (B, H);
+    its values are read on the device only."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    _check(o, "o", (B, H, T, d), None, dev)
+    _check(lse, "lse", (B, H, T), torch.float32, dev)
+    nd = _check_docs(cu_seqlens, dev)
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = library().fa_fwd_docs(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               B, H, T, d, c, int(bool(causal)), cu_seqlens.data_ptr(), nd, _dtype_code(q),
+                               _dtype_code(o), _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_fwd_docs")
+
+
+def fa_bwd_docs(q, k, v, o, do, lse, dq, dk, dv, cu_seqlens, workspace, *, scale=None, causal=False,
+                stream=None) -> None:
+    """Document-masked backward (bf16 inputs) into caller-provided dq, dk, dv."""
+    fa_bwd_docs_phases(q, k, v, o, do, lse, dq, dk, dv, cu_seqlens, workspace, FA_BWD_ALL, scale=scale,
+                       causal=causal, stream=stream)
+
+
+def fa_bwd_docs_phases(q, k, v, o, do, lse, dq, dk, dv, cu_seqlens, workspace, phases, *, scale=None,
+                       causal=False, stream=None) -> None:
+    """The named phases of the document-masked backward (an OR of FA_BWD_PRE, _MAIN, _POST)."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    _check(o, "o", (B, H, T, d), None, dev)
+    _check(lse, "lse", (B, H, T), torch.float32, dev)
+    _check(dq, "dq", (B, H, T, d), None, dev)
+    _check(dk, "dk", (B, H, T, d), dq.dtype, dev)
+    _check(dv, "dv", (B, H, T, d), dq.dtype, dev)
+    nd = _check_docs(cu_seqlens, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = library().fa_bwd_docs_phases(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, d, c,
+                                      int(bool(causal)), cu_seqlens.data_ptr(), nd, _dtype_code(q), _dtype_code(o),
+                                      _dtype_code(dq), workspace.data_ptr(), nbytes, int(phases),
+                                      _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_bwd_docs_phases")
+
+
 def forward(q, k, v, *, causal=False, scale=None, out_dtype=None, stream=None):
     """Allocate O and lse with torch and run fa_fwd.  Returns (O, lse).
 
@@ -448,4 +518,30 @@ def backward_window(q, k, v, o, do, lse, window, *, scale=None, grad_dtype=None,
         raise ValueError("invalid arguments for fa_bwd_window")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     fa_bwd_window(q, k, v, o, do, lse, dq, dk, dv, window, ws, scale=scale, stream=stream)
+    return dq, dk, dv
+
+
+def forward_docs(q, k, v, cu_seqlens, *, causal=False, scale=None, out_dtype=None, stream=None):
+    """Allocate O and lse with torch and run fa_fwd_docs.  Returns (O, lse)."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    o = torch.empty(q.shape, dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    fa_fwd_docs(q, k, v, o, lse, cu_seqlens, scale=scale, causal=causal, stream=stream)
+    return o, lse
+
+
+def backward_docs(q, k, v, o, do, lse, cu_seqlens, *, causal=False, scale=None, grad_dtype=None, stream=None):
+    """Allocate gradients and workspace with torch and run fa_bwd_docs.  Returns (dQ, dK, dV)."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty((B, H, T, d), dtype=gd, device=q.device)
+    dk = torch.empty((B, H, T, d), dtype=gd, device=q.device)
+    dv = torch.empty((B, H, T, d), dtype=gd, device=q.device)
+    nbytes = fa_bwd_workspace_bytes(B, H, T, T, d, _dtype_code(q), _dtype_code(dq))
+    if nbytes == 0:
+        raise ValueError("invalid arguments for fa_bwd_docs")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    fa_bwd_docs(q, k, v, o, do, lse, dq, dk, dv, cu_seqlens, ws, scale=scale, causal=causal, stream=stream)
     return dq, dk, dv

@@ -52,10 +52,20 @@ int window_mode(int wl, int wr, int* causal) {
   return !(wl < 0 && (wr < 0 || wr == 0));
 }
 
+// documents of a packed sequence: offsets cu_seqlens[0 .. ndocs] on the device
+int check_docs(const int* cu_seqlens, int ndocs, int dtype) {
+  if (!cu_seqlens) return FA_ERR_NULL;
+  if (ndocs < 1) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
              void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
              int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads, void* workspace,
-             size_t workspace_bytes, int phases, void* stream, int win = 0, int wl = 0, int wr = 0);
+             size_t workspace_bytes, int phases, void* stream, int band = 0, int wl = 0, int wr = 0,
+             const int* cu = nullptr, int nd = 0);
 
 }  // namespace
 
@@ -167,6 +177,37 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
                               dtype, o_dtype, grad_dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
 }
 
+int fa_fwd_docs(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int T, int d,
+                float scale, int causal, const int* cu_seqlens, int ndocs, int dtype, int out_dtype, void* stream) {
+  if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, T, T, d, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_docs(cu_seqlens, ndocs, dtype);
+  if (st != FA_OK) return st;
+  if (!valid_dtype(out_dtype)) return FA_ERR_DTYPE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse)) return FA_ERR_ALIGN;
+  return fa::launch_fwd_bf16(Q, K, V, O, lse, B, H, T, T, d, scale, causal ? 1 : 0, out_dtype == FA_F32 ? 1 : 0,
+                             static_cast<hipStream_t>(stream), nullptr, 1, 2, 0, 0, cu_seqlens, ndocs);
+}
+
+int fa_bwd_docs_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                       void* dQ, void* dK, void* dV, int B, int H, int T, int d, float scale, int causal,
+                       const int* cu_seqlens, int ndocs, int dtype, int o_dtype, int grad_dtype, void* workspace,
+                       size_t workspace_bytes, int phases, void* stream) {
+  const int st = check_docs(cu_seqlens, ndocs, dtype);
+  if (st != FA_OK) return st;
+  return bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, T, T, d, scale, causal, dtype, o_dtype, grad_dtype,
+                  nullptr, 1, workspace, workspace_bytes, phases, stream, 2, 0, 0, cu_seqlens, ndocs);
+}
+
+int fa_bwd_docs(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                void* dQ, void* dK, void* dV, int B, int H, int T, int d, float scale, int causal,
+                const int* cu_seqlens, int ndocs, int dtype, int o_dtype, int grad_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return fa_bwd_docs_phases(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, T, d, scale, causal, cu_seqlens, ndocs, dtype,
+                            o_dtype, grad_dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
 int fa_bwd_masked_phases(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                          const float* lse, void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d,
                          float scale, int causal, int dtype, int o_dtype, int grad_dtype,
@@ -192,7 +233,7 @@ namespace {
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
              void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal, int dtype,
              int o_dtype, int grad_dtype, const unsigned char* block_mask, int mask_heads, void* workspace,
-             size_t workspace_bytes, int phases, void* stream, int win, int wl, int wr) {
+             size_t workspace_bytes, int phases, void* stream, int band, int wl, int wr, const int* cu, int nd) {
   if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return FA_ERR_NULL;
   int st = check_common(B, H, Tq, Tk, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -214,7 +255,7 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
   if (dtype == FA_BF16)
     return fa::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal,
                                o_dtype == FA_F32 ? 1 : 0, grad_dtype == FA_F32 ? 1 : 0, workspace, phases, s,
-                               block_mask, mask_heads, win, wl, wr);
+                               block_mask, mask_heads, band, wl, wr, cu, nd);
   return fa::launch_bwd_f32(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, d, scale, causal, workspace, phases, s);
 }
 

@@ -43,14 +43,15 @@ constexpr int kTilesPerMaskRow = kMaskBlock / kBQ;
 static_assert(kBKC == kMaskBlock, "one key-block workgroup per mask column");
 
 // The query tiles a key-block sweep visits, shared by both key-block kernels:
-// all tiles from it0 on, or (masked) those whose 128-query block keeps this key
-// block.  count() is their number, next(t) the first visible tile >= t (nqt
-// when none is left).  Every lane of the wave must be active in both.
-template <bool MASKED, bool WIN = false>
+// all tiles from it0 on, those before nqe (band masks), or (block masks) those
+// whose 128-query block keeps this key block.  count() is their number, next(t)
+// the first visible tile >= t (nqt when none is left).  Every lane of the wave
+// must be active in both.
+template <bool MASKED, bool BANDED = false>
 struct KeyBlockTiles {
   const uint8_t* mcol;     // mask column of this key block (stride nmk), MASKED only
   int nmk, nmq, nvw, nqt, it0, lane;
-  int nqe = 0;             // WIN: one past the last query tile the window lets see the block
+  int nqe = 0;             // BANDED: one past the last query tile that sees the block
   int cw = -1;             // the word last read is kept in scalar registers
   unsigned long long cbits = 0;
 
@@ -77,7 +78,7 @@ struct KeyBlockTiles {
     return w * 64 + (int)__builtin_ctzll(bits);
   }
   __device__ int next(int t) {
-    if constexpr (WIN) return t < nqe ? t : nqt;
+    if constexpr (BANDED) return t < nqe ? t : nqt;
     if constexpr (MASKED) {
       if (t >= nqt) return nqt;
       if (row(t / kTilesPerMaskRow)) return t;
@@ -101,7 +102,7 @@ struct KeyBlockTiles {
       if (row(rlo)) n -= it0 - rlo * kTilesPerMaskRow;           // the first block starts at it0
       if (row(nmq - 1)) n -= nmq * kTilesPerMaskRow - nqt;       // the last block is ragged
       return n;
-    } else if constexpr (WIN) {
+    } else if constexpr (BANDED) {
       return max(0, nqe - it0);
     } else {
       return nqt - it0;
@@ -148,14 +149,14 @@ struct W4Layout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL, bool MASKED, bool WIN>
+template <int D, bool CAUSAL, bool MASKED, int BAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                       const float* __restrict__ Ln, const float* __restrict__ Dn,
                       void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e,
                       int nkb, int grad_f32, const uint8_t* __restrict__ bmask, int H, long long mask_hstride,
-                      int nmk, int wl, int wr) {
+                      int nmk, int wl, int wr, const int* __restrict__ cu, int nd, int bcausal) {
   using L = W4Layout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
@@ -197,9 +198,21 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     }
 
   const int nqt = (Tq + kBQ - 1) / kBQ;
-  const int it0 = WIN ? min(max(0, k0 - wr) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
-  KeyBlockTiles<MASKED, WIN> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
-  if constexpr (WIN) tiles.nqe = min(nqt, (min(k0 + kBKC, Tk) - 1 + wl) / kBQ + 1);
+  // BAND: the queries that see this block's keys, and those that see every key
+  // of this wave (a tile between them needs no element mask), from the key side
+  const Band<BAND> band{wl, wr, cu, nd, bcausal};
+  int w_qlo = 0, w_qhi = 0, my_qlo = 0, my_qhi = 0;   // and this lane's key: my_qlo .. my_qhi
+  if constexpr (BAND != 0) {
+    w_qlo = band.qlo(kw0 + kKeysPerWave - 1);
+    w_qhi = band.qhi(kw0);
+    band.queries(mykey, my_qlo, my_qhi);
+  }
+  const int it0 = BAND != 0 ? min(max(0, band.qlo(k0)) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
+  KeyBlockTiles<MASKED, BAND != 0> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  if constexpr (BAND != 0) {
+    const int qh = band.qhi(min(k0 + kBKC, Tk) - 1);
+    tiles.nqe = qh < 0 ? 0 : min(nqt, qh / kBQ + 1);
+  }
   const int n = tiles.count();                  // query tiles in the sweep
 
   // ---- staging of one query tile (Q_i, dO_i, Ln_i, Dn_i) ----
@@ -305,11 +318,11 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
       for (int r = 0; r < 16; ++r)
         if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
     }
-    if (WIN && !(kw0 >= r0 + kBQ - 1 - wl && kw0 + kKeysPerWave - 1 <= r0 + wr)) {   // crosses a band edge
+    if (BAND != 0 && !(r0 >= w_qlo && r0 + kBQ - 1 <= w_qhi)) {   // crosses a band edge
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = r0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (mykey < qr - wl || mykey > qr + wr) p[r] = 0.f;
+        if (qr < my_qlo || qr > my_qhi) p[r] = 0.f;
       }
     }
     bf16x8 pb[2], sbf[2];
@@ -471,12 +484,13 @@ struct KvLayout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL, bool MASKED, bool WIN>
+template <int D, bool CAUSAL, bool MASKED, int BAND>
 __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
     void* __restrict__ dK, void* __restrict__ dV, int Tq, int Tk, float scale, float cl2e, int nkb, int grad_f32,
-    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr) {
+    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr,
+    const int* __restrict__ cu, int nd, int bcausal) {
   using L = KvLayout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
@@ -494,13 +508,25 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   const int mykey = kw0 + l32;
 
   const int nqt = (Tq + kBQ - 1) / kBQ;
-  const int it0 = WIN ? min(max(0, k0 - wr) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
+  // BAND: the queries that see this block's keys, and those that see every key
+  // of this wave (a tile between them needs no element mask), from the key side
+  const Band<BAND> band{wl, wr, cu, nd, bcausal};
+  int w_qlo = 0, w_qhi = 0, my_qlo = 0, my_qhi = 0;   // and this lane's key: my_qlo .. my_qhi
+  if constexpr (BAND != 0) {
+    w_qlo = band.qlo(kw0 + kKeysPerWave - 1);
+    w_qhi = band.qhi(kw0);
+    band.queries(mykey, my_qlo, my_qhi);
+  }
+  const int it0 = BAND != 0 ? min(max(0, band.qlo(k0)) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
   // tile t covers query rows t kBQ ..; a tile past the sweep reads row Tq (zeros)
   auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
 
   // visible query tiles: all from it0 on, or (masked) those whose block keeps this key block
-  KeyBlockTiles<MASKED, WIN> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
-  if constexpr (WIN) tiles.nqe = min(nqt, (min(k0 + kBKC, Tk) - 1 + wl) / kBQ + 1);
+  KeyBlockTiles<MASKED, BAND != 0> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+  if constexpr (BAND != 0) {
+    const int qh = band.qhi(min(k0 + kBKC, Tk) - 1);
+    tiles.nqe = qh < 0 ? 0 : min(nqt, qh / kBQ + 1);
+  }
   const int n = tiles.count();                  // query tiles in the sweep
   auto next_tile = [&](int t) { return tiles.next(t); };
 
@@ -571,11 +597,11 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         for (int r = 0; r < 16; ++r)
           if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
       }
-      if (WIN && !(kw0 >= r0 + kBQ - 1 - wl && kw0 + kKeysPerWave - 1 <= r0 + wr)) {   // crosses a band edge
-#pragma unroll
+      if (BAND != 0 && !(r0 >= w_qlo && r0 + kBQ - 1 <= w_qhi)) {   // crosses a band edge
+  #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qr = r0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (mykey < qr - wl || mykey > qr + wr) p[r] = 0.f;
+          if (qr < my_qlo || qr > my_qhi) p[r] = 0.f;
         }
       }
       // fragments for the gradient wave: [P^T t=0, P^T t=1, dS^T t=0, dS^T t=1], 1 KiB each
@@ -797,13 +823,14 @@ __device__ __forceinline__ int dq_swz(int r) { return NC >= 16 ? (r & 15) : ((r 
 // rows.  Both rows go into LDS bitmaps (bit c = key block c visible); the
 // workgroup visits the key tiles that either row can see, and a wave computes
 // only those its own row can see.
-template <int D, bool CAUSAL, bool MASKED, bool WIN>
+template <int D, bool CAUSAL, bool MASKED, int BAND>
 __global__ __launch_bounds__(DqLayout<D>::THREADS)
 __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
     void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32,
-    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr) {
+    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr,
+    const int* __restrict__ cu, int nd, int bcausal) {
   using L = DqLayout<D>;
   constexpr int BC = L::BC;
   static_assert(kMaskBlock % BC == 0 && L::BR % kMaskBlock == 0 && L::BR <= 2 * kMaskBlock,
@@ -847,9 +874,19 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   int ntile = (Tk + BC - 1) / BC;
   if (CAUSAL) ntile = min(ntile, (min(q0 + L::BR, Tq) - 1) / BC + 1);
   int jfirst = 0;                                     // first key block any row of the block can see
-  if constexpr (WIN) {
-    ntile = min(ntile, (min(q0 + L::BR, Tq) - 1 + wr) / BC + 1);
-    jfirst = max(0, q0 - wl) / BC;
+  // BAND: this lane's keys klo .. khi; over the wave's rows, the keys every row
+  // sees (w_lo .. w_hi) and those some row sees (wb_lo .. wb_hi)
+  int klo = 0, khi = 0, w_lo = 0, w_hi = 0, wb_lo = 0, wb_hi = 0;
+  if constexpr (BAND != 0) {
+    const Band<BAND> band{wl, wr, cu, nd, bcausal};
+    band.keys(myq, klo, khi);
+    w_lo = band.lo(qw + 31);
+    w_hi = band.hi(qw);
+    wb_lo = band.lo(qw);
+    wb_hi = band.hi(qw + 31);
+    const int b_hi = band.hi(min(q0 + L::BR, Tq) - 1);
+    ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
+    jfirst = max(0, band.lo(q0)) / BC;
   }
 
   // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled
@@ -960,10 +997,10 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     t_load(first_row(jn));
     kv_dma(first_row(jn), ST ^ 1);
     const int kt0 = j * BC;
-    const bool in_band = !WIN || (kt0 <= qw + 31 + wr && kt0 + BC - 1 >= qw - wl);
+    const bool in_band = BAND == 0 || (kt0 <= wb_hi && kt0 + BC - 1 >= wb_lo);
     if ((!CAUSAL || kt0 <= qw + 31) && sees && in_band) {   // some key of the block is visible to this wave
       const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk) ||
-                        (WIN && !(kt0 >= qw + 31 - wl && kt0 + BC - 1 <= qw + wr));
+                        (BAND != 0 && !(kt0 >= w_lo && kt0 + BC - 1 <= w_hi));
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb) {
         // S^T and dP^T - D for 32 keys: register r = key kt0 + 32 kb + 8(r/4)+4hf+r%4, lane = query
@@ -990,7 +1027,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= Tk || (CAUSAL && key > myq) || (WIN && (key < myq - wl || key > myq + wr))) p[r] = 0.f;
+            if (key >= Tk || (CAUSAL && key > myq) || (BAND != 0 && (key < klo || key > khi))) p[r] = 0.f;
           }
         }
         bf16x8 sf[2];
@@ -1073,8 +1110,8 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 template <int D>
 int bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
         void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int o_f32, int grad_f32,
-        void* workspace, int phases, hipStream_t stream, const uint8_t* bmask, int mask_heads, int win, int wl,
-        int wr) {
+        void* workspace, int phases, hipStream_t stream, const uint8_t* bmask, int mask_heads, int band, int wl,
+        int wr, const int* cu, int nd) {
   using LQ = DqLayout<D>;
   const long long rows = (long long)B * H * Tq;
   const int nkb = (Tk + kBKC - 1) / kBKC;
@@ -1108,40 +1145,43 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
     constexpr int KV_THREADS = D == 256 ? 256 : 512;
     auto kv = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)nblk), dim3(KV_THREADS), 0, stream, q, k, v, g, Ln, Dn, dK, dV, Tq,
-                         Tk, scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk, wl, wr);
+                         Tk, scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
     };
     if constexpr (D == 256) {
-      if (win) kv(bwd_kv_w4_kernel<D, false, false, true>);
+      if (band == 1) kv(bwd_kv_w4_kernel<D, false, false, 1>);
+      else if (band == 2) kv(bwd_kv_w4_kernel<D, false, false, 2>);
       else if (bmask) {
-        if (causal) kv(bwd_kv_w4_kernel<D, true, true, false>);
-        else kv(bwd_kv_w4_kernel<D, false, true, false>);
+        if (causal) kv(bwd_kv_w4_kernel<D, true, true, 0>);
+        else kv(bwd_kv_w4_kernel<D, false, true, 0>);
       } else {
-        if (causal) kv(bwd_kv_w4_kernel<D, true, false, false>);
-        else kv(bwd_kv_w4_kernel<D, false, false, false>);
+        if (causal) kv(bwd_kv_w4_kernel<D, true, false, 0>);
+        else kv(bwd_kv_w4_kernel<D, false, false, 0>);
       }
     } else {
-      if (win) kv(bwd_kv_kernel<D, false, false, true>);
+      if (band == 1) kv(bwd_kv_kernel<D, false, false, 1>);
+      else if (band == 2) kv(bwd_kv_kernel<D, false, false, 2>);
       else if (bmask) {
-        if (causal) kv(bwd_kv_kernel<D, true, true, false>);
-        else kv(bwd_kv_kernel<D, false, true, false>);
+        if (causal) kv(bwd_kv_kernel<D, true, true, 0>);
+        else kv(bwd_kv_kernel<D, false, true, 0>);
       } else {
-        if (causal) kv(bwd_kv_kernel<D, true, false, false>);
-        else kv(bwd_kv_kernel<D, false, false, false>);
+        if (causal) kv(bwd_kv_kernel<D, true, false, 0>);
+        else kv(bwd_kv_kernel<D, false, false, 0>);
       }
     }
   }
   if (phases & FA_BWD_POST) {
     auto dqk = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)nqblk), dim3(LQ::THREADS), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq,
-                         Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr);
+                         Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
     };
-    if (win) dqk(bwd_dq_kernel<D, false, false, true>);
+    if (band == 1) dqk(bwd_dq_kernel<D, false, false, 1>);
+    else if (band == 2) dqk(bwd_dq_kernel<D, false, false, 2>);
     else if (bmask) {
-      if (causal) dqk(bwd_dq_kernel<D, true, true, false>);
-      else dqk(bwd_dq_kernel<D, false, true, false>);
+      if (causal) dqk(bwd_dq_kernel<D, true, true, 0>);
+      else dqk(bwd_dq_kernel<D, false, true, 0>);
     } else {
-      if (causal) dqk(bwd_dq_kernel<D, true, false, false>);
-      else dqk(bwd_dq_kernel<D, false, false, false>);
+      if (causal) dqk(bwd_dq_kernel<D, true, false, 0>);
+      else dqk(bwd_dq_kernel<D, false, false, 0>);
     }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -1152,11 +1192,11 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                     int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream, const uint8_t* bmask,
-                    int mask_heads, int win, int wl, int wr) {
+                    int mask_heads, int band, int wl, int wr, const int* cu, int nd) {
   switch (d) {
-    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, win, wl, wr);
-    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, win, wl, wr);
-    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, win, wl, wr);
+    case 64: return bwd<64>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, band, wl, wr, cu, nd);
+    case 128: return bwd<128>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, band, wl, wr, cu, nd);
+    case 256: return bwd<256>(Q, K, V, O, dO, lse, dQ, dK, dV, B, H, Tq, Tk, scale, causal, o_f32, grad_f32, workspace, phases, stream, bmask, mask_heads, band, wl, wr, cu, nd);
     default: return FA_ERR_HEADDIM;
   }
 }

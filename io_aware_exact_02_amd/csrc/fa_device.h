@@ -110,4 +110,66 @@ __device__ __forceinline__ unsigned long long mask_word(const uint8_t* m, long l
   return __ballot(i < n && m[(long long)i * stride] != 0);
 }
 
+// The document of position x in a packed sequence: the largest i < n with
+// cu[i] <= x, for offsets cu[0] = 0 <= cu[1] <= ... <= cu[n] of n documents.
+// Reads cu[0 .. n-1] only; works for a wave-uniform or a per-lane x.
+__device__ __forceinline__ int doc_of(const int* cu, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// A band mask: query r sees the keys lo(r) .. hi(r) and key l is seen by the
+// queries qlo(l) .. qhi(l), all four non-decreasing.  KIND 1 is a sliding
+// window, r - wl <= l <= r + wr (an unbounded side arrives as a large number);
+// KIND 2 the documents of a packed sequence with offsets cu[0 .. nd], r and l
+// in one document and, when causal, l <= r.
+template <int KIND>
+struct Band {
+  int wl, wr;
+  const int* cu;
+  int nd, causal;
+  __device__ int lo(int r) const {
+    if constexpr (KIND == 1) return r - wl;
+    else return cu[doc_of(cu, nd, r)];
+  }
+  __device__ int hi(int r) const {
+    if constexpr (KIND == 1) return r + wr;
+    else return causal ? r : cu[doc_of(cu, nd, r) + 1] - 1;
+  }
+  __device__ int qlo(int l) const {
+    if constexpr (KIND == 1) return l - wr;
+    else return causal ? l : cu[doc_of(cu, nd, l)];
+  }
+  __device__ int qhi(int l) const {
+    if constexpr (KIND == 1) return l + wl;
+    else return cu[doc_of(cu, nd, l) + 1] - 1;
+  }
+  // both ends with one search: the keys of query r, the queries of key l
+  __device__ void keys(int r, int& a, int& b) const {
+    if constexpr (KIND == 1) {
+      a = r - wl;
+      b = r + wr;
+    } else {
+      const int i = doc_of(cu, nd, r);
+      a = cu[i];
+      b = causal ? r : cu[i + 1] - 1;
+    }
+  }
+  __device__ void queries(int l, int& a, int& b) const {
+    if constexpr (KIND == 1) {
+      a = l - wr;
+      b = l + wl;
+    } else {
+      const int i = doc_of(cu, nd, l);
+      a = causal ? l : cu[i];
+      b = cu[i + 1] - 1;
+    }
+  }
+};
+
 }  // namespace fa

@@ -81,15 +81,16 @@ struct FwdLayout {
 template <int NC>
 __device__ __forceinline__ int kswz(int r) { return NC >= 16 ? (r & 15) : ((r >> 1) & 7); }
 
-// WIN: sliding window, key l visible from query r iff r - wl <= l <= r + wr (an
-// unbounded side arrives as a large number), with tiles outside the band of
-// the block never visited and elements masked only on tiles crossing its edges.
-template <int D, bool CAUSAL, bool OUT_F32, bool MASKED, bool WIN>
+// BAND (1 sliding window, 2 documents): each query row r sees the keys
+// lo(r) .. hi(r) of a Band, both non-decreasing in r.  Key blocks outside the block's band are never visited; elements are masked
+// only on tiles that cross a band edge of some row of the wave.
+template <int D, bool CAUSAL, bool OUT_F32, bool MASKED, int BAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_EU)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, void* __restrict__ O,
                      float* __restrict__ lse, int Tq, int Tk, float cl2e, int nqb,
-                     const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr) {
+                     const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr,
+                     const int* __restrict__ cu, int nd, int bcausal) {
   using L = FwdLayout<D>;
   constexpr int BC = L::BC;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
@@ -126,9 +127,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   int ntile = (Tk + BC - 1) / BC;
   if (CAUSAL) ntile = min(ntile, (min(q0 + kBR, Tq) - 1) / BC + 1);
   int jfirst = 0;                     // first key block any row of the block can see
-  if constexpr (WIN) {
-    ntile = min(ntile, (min(q0 + kBR - 1, Tq - 1) + wr) / BC + 1);
-    jfirst = max(0, q0 - wl) / BC;
+  // BAND: this lane's keys klo .. khi; over the wave's rows the largest lo and
+  // the smallest hi (a tile between them needs no element mask)
+  int klo = 0, khi = 0, w_lo = 0, w_hi = 0;
+  if constexpr (BAND != 0) {
+    const Band<BAND> band{wl, wr, cu, nd, bcausal};
+    band.keys(myq, klo, khi);
+    w_lo = band.lo(qw + 31);
+    w_hi = band.hi(qw);
+    const int b_hi = band.hi(min(q0 + kBR, Tq) - 1);
+    ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
+    jfirst = max(0, band.lo(q0)) / BC;
   }
 
   // ---- K: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
@@ -205,15 +214,15 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
   auto mask_tile = [&](f32x16 (&s)[L::NKB], int j) {
     const int k0 = j * BC;
-    if constexpr (WIN) {
-      // inside the band for every row of the wave: no element mask needed
-      if (k0 >= qw + 31 - wl && k0 + BC - 1 <= qw + wr && k0 + BC <= Tk) return;
+    if constexpr (BAND != 0) {
+      // inside the band of every row of the wave: no element mask needed
+      if (k0 >= w_lo && k0 + BC - 1 <= w_hi && k0 + BC <= Tk) return;
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= Tk || key < myq - wl || key > myq + wr) s[kb][r] = -INFINITY;
+          if (key >= Tk || key < klo || key > khi) s[kb][r] = -INFINITY;
         }
       return;
     }
@@ -369,8 +378,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const float l_tot = half_swap_sum(l_part);
   const float lr_tot = half_swap_sum(lr_part);
   if (myq >= Tq) return;
-  // a row that sees no key (possible only under a block mask or a window) gets O = 0, lse = -inf
-  const float inv = (!(MASKED || WIN) || lr_tot > 0.f) ? 1.f / lr_tot : 0.f;
+  // a row that sees no key (possible only under a block mask or a band) gets O = 0, lse = -inf
+  const float inv = (!(MASKED || BAND != 0) || lr_tot > 0.f) ? 1.f / lr_tot : 0.f;
 #pragma unroll
   for (int db = 0; db < L::NDB; ++db)
 #pragma unroll
@@ -388,15 +397,15 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       }
     }
   if (hf == 0)
-    lse[(size_t)bh * Tq + myq] = (!(MASKED || WIN) || l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    lse[(size_t)bh * Tq + myq] = (!(MASKED || BAND != 0) || l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32, bool MASKED, bool WIN>
+template <int D, bool CAUSAL, bool OUT_F32, bool MASKED, int BAND>
 void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                 float* lse, int Tq, int Tk, float cl2e, int nqb, const uint8_t* bmask, int H, long long hstride,
-                int nmk, int wl, int wr) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, MASKED, WIN>), grid, dim3(256), 0, stream, q, k, v, o, lse,
-                     Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk, wl, wr);
+                int nmk, int wl = 0, int wr = 0, const int* cu = nullptr, int nd = 0, int bcausal = 0) {
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, MASKED, BAND>), grid, dim3(256), 0, stream, q, k, v, o, lse,
+                     Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk, wl, wr, cu, nd, bcausal);
 }
 
 template <int D, bool MASKED>
@@ -404,18 +413,18 @@ void launch_dtype(dim3 grid, hipStream_t stream, int causal, int out_f32, const 
                   const uint16_t* v, void* O, float* lse, int Tq, int Tk, float cl2e, int nqb, const uint8_t* bmask,
                   int H, long long hstride, int nmk) {
   if (causal) {
-    if (out_f32) launch_one<D, true, true, MASKED, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk, 0, 0);
-    else launch_one<D, true, false, MASKED, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk, 0, 0);
+    if (out_f32) launch_one<D, true, true, MASKED, 0>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+    else launch_one<D, true, false, MASKED, 0>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
   } else {
-    if (out_f32) launch_one<D, false, true, MASKED, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk, 0, 0);
-    else launch_one<D, false, false, MASKED, false>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk, 0, 0);
+    if (out_f32) launch_one<D, false, true, MASKED, 0>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+    else launch_one<D, false, false, MASKED, 0>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
   }
 }
 
 template <int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq, int Tk,
-           float scale, int causal, int out_f32, const uint8_t* bmask, int mask_heads, int win, int wl, int wr,
-           hipStream_t stream) {
+           float scale, int causal, int out_f32, const uint8_t* bmask, int mask_heads, int band, int wl, int wr,
+           const int* cu, int nd, hipStream_t stream) {
   const int nqb = (Tq + kBR - 1) / kBR;
   const long long nblk = (long long)nqb * B * H;
   if (nblk > 0x7fffffffLL) return FA_ERR_SHAPE;
@@ -427,11 +436,18 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int
   // block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)]; the 128-row blocks are this kernel's query blocks
   const int nmk = (Tk + 127) / 128;
   const long long hstride = mask_heads == 1 ? 0 : (long long)nqb * nmk;
-  if (win) {
+  if (band == 1) {
     if (out_f32)
-      launch_one<D, false, true, false, true>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
+      launch_one<D, false, true, false, 1>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
     else
-      launch_one<D, false, false, false, true>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
+      launch_one<D, false, false, false, 1>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
+  } else if (band == 2) {
+    if (out_f32)
+      launch_one<D, false, true, false, 2>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, 0, 0, cu,
+                                           nd, causal);
+    else
+      launch_one<D, false, false, false, 2>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, 0, 0, cu,
+                                            nd, causal);
   } else if (bmask) {
     launch_dtype<D, true>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
   } else {
@@ -444,11 +460,11 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int
 
 int launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H,
                     int Tq, int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream,
-                    const uint8_t* bmask, int mask_heads, int win, int wl, int wr) {
+                    const uint8_t* bmask, int mask_heads, int band, int wl, int wr, const int* cu, int nd) {
   switch (d) {
-    case 64: return launch<64>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, win, wl, wr, stream);
-    case 128: return launch<128>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, win, wl, wr, stream);
-    case 256: return launch<256>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, win, wl, wr, stream);
+    case 64: return launch<64>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, band, wl, wr, cu, nd, stream);
+    case 128: return launch<128>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, band, wl, wr, cu, nd, stream);
+    case 256: return launch<256>(Q, K, V, O, lse, B, H, Tq, Tk, scale, causal, out_f32, bmask, mask_heads, band, wl, wr, cu, nd, stream);
     default: return FA_ERR_HEADDIM;
   }
 }

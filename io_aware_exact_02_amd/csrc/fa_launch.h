@@ -10,17 +10,21 @@ namespace fa {
 inline long long bwd_rows_padded(long long rows) { return (rows + 63) / 64 * 64; }
 
 // bmask: optional block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)] (uint8, device memory)
-// win != 0: sliding window, key l visible from query r iff r - wl <= l <= r + wr
-// (wl, wr >= 0; an unbounded side is passed as a large value)
+// band 1: sliding window, key l visible from query r iff r - wl <= l <= r + wr
+// (wl, wr >= 0; an unbounded side is passed as a large value).  band 2:
+// documents of a packed sequence, offsets cu[0..nd] on the device, causal
+// within each document when causal != 0.
 int launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
                     int Tk, int d, float scale, int causal, int out_f32, hipStream_t stream,
-                    const uint8_t* bmask = nullptr, int mask_heads = 1, int win = 0, int wl = 0, int wr = 0);
+                    const uint8_t* bmask = nullptr, int mask_heads = 1, int band = 0, int wl = 0, int wr = 0,
+                    const int* cu = nullptr, int nd = 0);
 int launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* lse, int B, int H, int Tq,
                    int Tk, int d, float scale, int causal, hipStream_t stream);
 int launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                     void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                     int o_f32, int grad_f32, void* workspace, int phases, hipStream_t stream,
-                    const uint8_t* bmask = nullptr, int mask_heads = 1, int win = 0, int wl = 0, int wr = 0);
+                    const uint8_t* bmask = nullptr, int mask_heads = 1, int band = 0, int wl = 0, int wr = 0,
+                    const int* cu = nullptr, int nd = 0);
 int launch_bwd_f32(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
                    void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int causal,
                    void* workspace, int phases, hipStream_t stream);

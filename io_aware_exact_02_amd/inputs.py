@@ -15,6 +15,10 @@ drawn as Bernoulli(density) per block from `default_rng(seed)` in row-major
 order (uniform draws < density), after which the listed forced blocks are set:
 the diagonal (i, i) when `keep_diagonal`, so that every query block sees at
 least one key block, and the rows in `empty_rows` cleared.
+
+Documents (packed sequences): offsets int32 [ndocs + 1] from `default_rng(seed)`,
+each document's length exp(U(ln lo, ln hi)) rounded to the nearest integer, laid
+end to end from 0 until they reach T, the last one cut at T.
 """
 from __future__ import annotations
 
@@ -56,6 +60,7 @@ class Workload:
     seed: int = BASE_SEED
     mask_density: float | None = None   # block-sparse: fraction of kept 128 x 128 blocks (one mask per head)
     window: tuple | None = None         # sliding window (wl, wr): keys r - wl .. r + wr of query r
+    doc_len: tuple | None = None        # packed documents: lengths log-uniform in [lo, hi]
 
     def flops_fwd(self) -> float:
         """4 B H Tq Tk d, halved when causal (square causal: visible pairs ~ T^2 / 2)."""
@@ -86,6 +91,9 @@ WORKLOADS = {
     # sliding window: 4096 keys up to and including the query's own (window (4095, 0))
     "swa_bf16_b1h32_t32768_d128_w4096": Workload("swa_bf16_b1h32_t32768_d128_w4096", 1, 32, 32768, 32768, 128,
                                                  "bf16", False, True, seed=BASE_SEED + 8, window=(4095, 0)),
+    # packed documents: 32768 tokens of documents 64 .. 8192 long, causal within each
+    "docs_bf16_b1h32_t32768_d128": Workload("docs_bf16_b1h32_t32768_d128", 1, 32, 32768, 32768, 128, "bf16",
+                                            True, True, seed=BASE_SEED + 9, doc_len=(64, 8192)),
     # decoding: one query row per head against a long key cache (split-key forward)
     "decode_bf16_b8h16_tq1_tk32768_d128": Workload("decode_bf16_b8h16_tq1_tk32768_d128", 8, 16, 1, 32768, 128,
                                                    "bf16", False, False, seed=BASE_SEED + 6),
@@ -138,3 +146,18 @@ def workload_mask(w: Workload, density=None):
     """The block mask of a block-sparse workload: one per head, seeded from the workload
     (`density` overrides the workload's own, for sweeps)."""
     return block_mask(w.H, w.Tq, w.Tk, w.mask_density if density is None else density, w.seed + 1000)
+
+
+def doc_offsets(T, lo, hi, seed):
+    """Seeded document offsets int32 [ndocs + 1] covering 0 .. T (recipe above)."""
+    rng = np.random.default_rng(seed)
+    cu = [0]
+    while cu[-1] < T:
+        n = int(np.rint(np.exp(rng.uniform(np.log(lo), np.log(hi)))))
+        cu.append(min(T, cu[-1] + max(1, n)))
+    return np.asarray(cu, dtype=np.int32)
+
+
+def workload_docs(w: Workload):
+    """The document offsets of a packed-document workload, seeded from the workload."""
+    return doc_offsets(w.Tq, w.doc_len[0], w.doc_len[1], w.seed + 2000)

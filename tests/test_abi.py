@@ -232,3 +232,30 @@ def test_window_argument_errors(lib):
     assert bwd(ws=None) == WORKSPACE
     assert bwd(phases=8) == PHASE
     assert bwd(phases=0) == OK              # checks only, launches nothing
+
+
+def test_docs_argument_errors(lib):
+    def fwd(cu=P, nd=3, dtype=fa.FA_BF16, odtype=fa.FA_BF16, d=128, T=300, null_at=None):
+        ptrs = [P] * 5
+        if null_at is not None:
+            ptrs[null_at] = None
+        return lib.fa_fwd_docs(*ptrs, 1, 2, T, d, 0.125, 1, cu, nd, dtype, odtype, None)
+
+    def bwd(cu=P, nd=3, dtype=fa.FA_BF16, ws=P, ws_bytes=1 << 30, phases=None):
+        args = [P] * 9 + [1, 2, 300, 128, 0.125, 0, cu, nd, dtype, dtype, dtype, ws, ws_bytes]
+        if phases is None:
+            return lib.fa_bwd_docs(*args, None)
+        return lib.fa_bwd_docs_phases(*args, phases, None)
+
+    for i in range(5):
+        assert fwd(null_at=i) == NULL
+    assert fwd(cu=None) == NULL and bwd(cu=None) == NULL
+    for nd in (0, -1):
+        assert fwd(nd=nd) == SHAPE and bwd(nd=nd) == SHAPE
+    assert fwd(T=0) == SHAPE
+    assert fwd(cu=P + 2) == ALIGN and bwd(cu=P + 2) == ALIGN
+    assert fwd(dtype=fa.FA_F32, odtype=fa.FA_F32) == DTYPE and bwd(dtype=fa.FA_F32) == DTYPE
+    assert fwd(d=96) == HEADDIM
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(phases=8) == PHASE
+    assert bwd(phases=0) == OK              # checks only, launches nothing
