@@ -47,6 +47,22 @@ __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives as its
+// element e (e = 0..3) the 16-bit element i % 4 of the 8 bytes addressed by lane
+// 4e + i / 4 of the group.  When the lanes of a group address four consecutive
+// rows of a row-major tile (four lanes per row, 4 columns each), every lane gets
+// one column of those four rows: the transposed operand of an MFMA.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ld8_tr(const void* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// NaN-propagating maxima (v_maximum3_f32 on gfx950: no canonicalising moves).
+__device__ __forceinline__ float max2f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return max2f(max2f(a, b), c); }
+
 // Round two floats to bf16 (nearest-even; one v_cvt_pk_bf16_f32) packed low|high.
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   f32x2 v = {lo, hi};

@@ -11,9 +11,9 @@
 //     lane l of a load lands at LDS base + 16 l, so the 16-byte chunks of a K
 //     row are placed XOR-swizzled by row, which makes the MFMA operand reads
 //     below conflict-free without padding.  Rows past Tk read as zeros.
-//   * V_j goes HBM -> registers (16-byte buffer loads) -> LDS transposed
-//     (4x8 bf16 blocks repacked in registers), so the PV product's operand is
-//     one ds_read_b128 per MFMA as well.
+//   * V_j goes HBM -> LDS the same way, row-major with its own chunk swizzle;
+//     the PV product reads its transposed operand (one feature per lane, 8
+//     keys) with two transposing 8-byte LDS reads per MFMA, conflict-free.
 // Products (32x32x16 bf16 MFMA, float32 accumulation):
 //   * S^T = K_j Q^T puts one query row per lane (its other half in lane ^ 32):
 //     the row maximum and sum are register reductions plus a v_permlane32_swap.
@@ -30,9 +30,8 @@
 // above the diagonal are never loaded ([ZtF] "The causal mask, and the tiles
 // you never visit": the sweep stops at the block's last query).
 //
-// One barrier per block: block j's S, softmax and PV run while K_{j+1} (into
-// the other LDS stage) and V_{j+1} (into registers) are in flight from HBM;
-// V_{j+1} is repacked into LDS at the end.  On gfx950 the MFMA and vector-ALU
+// One barrier per block: block j's S, softmax and PV run while K_{j+1} and
+// V_{j+1} are in flight from HBM into the other LDS stage.  On gfx950 the MFMA and vector-ALU
 // work of a SIMD do not overlap in time (the second wave on the SIMD covers
 // latencies), so the softmax is kept to as few vector instructions per score
 // as possible.
@@ -57,22 +56,19 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 template <int D>
 struct FwdLayout {
   static constexpr int BC = FwdCfg<D>::BC;
-  static constexpr int NC = D / 8;                   // 16-byte chunks per K row
-  static constexpr int KST = BC * D * 2;             // bytes per K stage (unpadded, swizzled)
-  static constexpr int VSTR = BC + 8;                // bf16 per V^T row (16-byte pad)
-  static constexpr int VST = D * VSTR * 2;           // bytes per V^T stage
-  static constexpr int BYTES = 2 * KST + 2 * VST;
+  static constexpr int NC = D / 8;                   // 16-byte chunks per K / V row
+  static constexpr int RB = D * 2;                   // bytes per row
+  static constexpr int KST = BC * RB;                // bytes per K (or V) stage (unpadded, swizzled)
+  static constexpr int BYTES = 4 * KST;
   static constexpr int NKB = BC / 32;                // 32-key MFMA blocks per tile
   static constexpr int NDB = D / 32;                 // 32-feature output blocks
   static constexpr int NDS = D / 16;                 // k-steps of the QK^T product
-  static constexpr int KDMA = KST / 1024;            // 1 KB LDS-load instructions per K tile
+  static constexpr int KDMA = KST / 1024;            // 1 KB LDS-load instructions per K (or V) tile
   static constexpr int KDMA_W = KDMA / kWaves;       // ... per wave
-  static constexpr int NVB = (BC / 4) * (D / 8);     // 4x8 V blocks per tile
   static_assert(KDMA % kWaves == 0, "K tile must split evenly over the waves");
-  static_assert(NVB <= 256, "one V block per thread at most");
   static_assert(NC == 8 || NC >= 16, "swizzle assumes 8 or >= 16 chunks per row");
   static constexpr int k_off(int st) { return st * KST; }
-  static constexpr int v_off(int st) { return 2 * KST + st * VST; }
+  static constexpr int v_off(int st) { return (2 + st) * KST; }
 };
 
 // Chunk swizzle of K row r: with 16 or more chunks per row the 16 rows a
@@ -80,6 +76,14 @@ struct FwdLayout {
 // (128-byte rows, two per 256-byte bank cycle) rows pair up by r >> 1.
 template <int NC>
 __device__ __forceinline__ int kswz(int r) { return NC >= 16 ? (r & 15) : ((r >> 1) & 7); }
+
+// Chunk swizzle of V row r, for the transposing reads: a half-wave reads four
+// consecutive rows x four chunks (8 bytes per lane), and XOR-ing the chunk's
+// bits 2-3 with the row's position among the four (bit 2 with the row pair for
+// 128-byte rows) puts those 32 reads on 64 distinct banks.  The swizzle only
+// moves chunk bits >= 2, so a feature block's offset is a XOR with (db << 6).
+template <int NC>
+__device__ __forceinline__ int vswz(int r) { return NC == 8 ? 4 * ((r >> 1) & 1) : 4 * (r & 3); }
 
 // BAND (1 sliding window, 2 documents): each query row r sees the keys
 // lo(r) .. hi(r) of a Band, both non-decreasing in r.  Key blocks outside the block's band are never visited; elements are masked
@@ -140,7 +144,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     jfirst = max(0, band.lo(q0)) / BC;
   }
 
-  // ---- K: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
+  // ---- K and V: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
   auto k_dma = [&](int k0, int kst_off) {
 #pragma unroll
     for (int i = 0; i < L::KDMA_W; ++i) {
@@ -153,38 +157,33 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           rk, (__attribute__((address_space(3))) void*)(smem + kst_off + g * 1024), 16, off, 0, 0, 0);
     }
   };
+  auto v_dma = [&](int k0, int vst_off) {
+#pragma unroll
+    for (int i = 0; i < L::KDMA_W; ++i) {
+      const int g = wave * L::KDMA_W + i;
+      const int s = g * 64 + lane;
+      const int row = s / L::NC, cp = s % L::NC;
+      const int src = cp ^ vswz<L::NC>(row);
+      const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(smem + vst_off + g * 1024), 16, off, 0, 0, 0);
+    }
+  };
   // Per-lane K read offset (bytes, relative to a stage and a 32-key block) for
   // k-step ds: chunk (2 ds + hf) ^ swz of row lq.  The XOR only touches bits 5..7
   // of kbase_lane (rows are >= 128 bytes), so each k-step is kbase_lane ^ (ds << 5).
   const int kswz_l = kswz<L::NC>(lq);
   const int kbase_lane = lq * D * 2 + (((kswz_l >> 1) << 5) | ((hf ^ (kswz_l & 1)) << 4));
 
-  // ---- V: HBM -> registers -> LDS transposed (4 keys x 8 features per thread).
-  const bool v_loader = tid < L::NVB;
-  const int kq = tid % (BC / 4), dg = tid / (BC / 4);
-  // position of key quad kq in its V^T row: the middle quads of each 16 keys are
-  // swapped so the 8 keys an MFMA k-slot half needs are contiguous
-  const int kq3 = kq & 3;
-  const int vpos = 16 * (kq >> 2) + 4 * (kq3 == 1 ? 2 : (kq3 == 2 ? 1 : kq3));
-  u32x4 vst[4];
-  auto v_load = [&](int k0) {
-    if (v_loader) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vst[i] = bload16(rv, ((unsigned)(k0 + 4 * kq + i) * D + dg * 8) * 2u);
-    }
-  };
-  auto v_store = [&](int vst_off) {
-    if (v_loader) {
-      char* base = smem + vst_off + (dg * 8 * L::VSTR + vpos) * 2;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x2 even = {lo_lo(vst[0][w], vst[1][w]), lo_lo(vst[2][w], vst[3][w])};
-        const u32x2 odd = {hi_hi(vst[0][w], vst[1][w]), hi_hi(vst[2][w], vst[3][w])};
-        st8(base + (2 * w) * L::VSTR * 2, even);
-        st8(base + (2 * w + 1) * L::VSTR * 2, odd);
-      }
-    }
-  };
+  // ---- V^T operand (A of O^T += V^T P^T): lane l, row feature 32 db + l % 32,
+  // elements = keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3 of key block kb,
+  // the order of the P fragment's k-slots.  Each comes from one transposing read
+  // in which lane 16g + 4e + j addresses key row 4(g/2) + e and features
+  // 16(g%2) + 4j .. +3 (plus 32kb + 16t, and 8 for the second read).
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vrow = 4 * (vg >> 1) + (vi >> 2);
+  const int vc0 = 2 * (vg & 1) + ((vi & 3) >> 1);
+  const int vlane = vrow * L::RB + ((vc0 ^ vswz<L::NC>(vrow)) << 4) + 8 * (vi & 1);
 
   f32x16 o[L::NDB];
 #pragma unroll
@@ -277,16 +276,15 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
   const int j0 = next_tile(jfirst);
   k_dma(first_row(j0), L::k_off(0));
-  v_load(first_row(j0));
-  v_store(L::v_off(0));
+  v_dma(first_row(j0), L::v_off(0));
   wait_vmem_all();
   __syncthreads();
 
   auto step = [&](int j, int jn, auto stage) {
     constexpr int ST = decltype(stage)::value;        // position of block j in the sweep, mod 2
-    // the next visited block jn in flight: K straight into LDS, V into registers
-    v_load(first_row(jn));
+    // the next visited block jn in flight, straight into the other LDS stage
     k_dma(first_row(jn), L::k_off(ST ^ 1));
+    v_dma(first_row(jn), L::v_off(ST ^ 1));
     f32x16 s[L::NKB];
     s_product(s, L::k_off(ST));
     mask_tile(s, j);
@@ -294,13 +292,22 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // results: long chains of dependent vector ops leave the wave stalled
     float mq[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) mq[q] = fmaxf(fmaxf(s[0][4 * q], s[0][4 * q + 1]), fmaxf(s[0][4 * q + 2], s[0][4 * q + 3]));
+    for (int q = 0; q < 4; ++q) {
+      // chain q folds s[kb][4q .. 4q+3] for every kb, two new values per max3
+      float m = max3f(s[0][4 * q], s[0][4 * q + 1], s[0][4 * q + 2]);
+      float pend = s[0][4 * q + 3];
+      bool has = true;
 #pragma unroll
-    for (int kb = 1; kb < L::NKB; ++kb)
+      for (int kb = 1; kb < L::NKB; ++kb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        mq[q] = fmaxf(mq[q], fmaxf(fmaxf(s[kb][4 * q], s[kb][4 * q + 1]), fmaxf(s[kb][4 * q + 2], s[kb][4 * q + 3])));
-    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+        for (int e = 0; e < 4; ++e) {
+          if (has) m = max3f(m, pend, s[kb][4 * q + e]);
+          else pend = s[kb][4 * q + e];
+          has = !has;
+        }
+      mq[q] = has ? max2f(m, pend) : m;
+    }
+    float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
     mx = half_swap_max(mx) * cl2e;
     const bool grow = mx > m_ref + kRescaleSlack;     // never true for a row with no visible key yet
     if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
@@ -343,16 +350,18 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int db = 0; db < L::NDB; ++db)
-          va[kb][t][db] = as_bf16x8(ld16(vs + ((db * 32 + lq) * L::VSTR + kb * 32 + 16 * t + 8 * hf) * 2));
+        for (int db = 0; db < L::NDB; ++db) {
+          const char* p = vs + (32 * kb + 16 * t) * L::RB + (vlane ^ (db << 6));
+          const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
+          va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
 #pragma unroll
     for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
-    sched_reads_ahead<L::NKB * 2 * L::NDB>();
-    v_store(L::v_off(ST ^ 1));
+    sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
     wait_vmem_all();
     __syncthreads();
   };
