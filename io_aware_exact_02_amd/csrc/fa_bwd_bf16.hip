@@ -776,8 +776,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 // over key blocks of 64 keys (32 for d = 256) -- causal: up to the block's
 // last query; tiles a wave cannot see are skipped by that wave.  Per key block j:
 //   * K_j and V_j go HBM -> LDS by buffer_load ... lds (rows XOR-swizzled by
-//     16-byte chunk); K_j^T goes HBM -> registers -> LDS transposed, its key
-//     order matching the k-slot order of the dS fragments below.
+//     16-byte chunk).  K_j serves both products: row reads for S^T, and
+//     transposing 8-byte reads (one feature per lane, keys in the k-slot order
+//     of the dS fragments) for K_j^T.
 //   * S^T = K_j Q^T and dP^T - D = V_j dO^T - D on MFMA put one query per lane,
 //     so lse and D are per-lane constants (-D seeds the accumulator):
 //     P^T = exp2(S^T c log2e - lse log2e) and dS^T = P^T * (dP^T - D) ([ZtF]
@@ -793,31 +794,40 @@ struct DqLayout {
   static constexpr int BR = 32 * WAVES;                // query rows per workgroup
   static constexpr int BC = D == 256 ? 32 : 64;        // keys per block
   static constexpr int NC = D / 8;                     // 16-byte chunks per K/V row
-  static constexpr int KST = BC * D * 2;               // K (or V) tile, swizzled rows, unpadded
-  static constexpr int TSTR = BC + 8;                  // bf16 per K^T row (16-byte pad)
-  static constexpr int TST = D * TSTR * 2;
-  static constexpr int STAGE = 2 * KST + TST;
+  static constexpr int RB = D * 2;                     // bytes per K/V row
+  static constexpr int KST = BC * RB;                  // K (or V) tile, swizzled rows, unpadded
+  static constexpr int STAGE = 2 * KST;
   static constexpr int BYTES = 2 * STAGE;
   static constexpr int NKB = BC / 32;
   static constexpr int NDB = D / 32;
   static constexpr int NDS = D / 16;
   static constexpr int KDMA = KST / 1024;              // 1 KiB DMA instructions per K (or V) tile
   static constexpr int KDMA_W = 2 * KDMA / WAVES;      // per wave: the first half of the waves load K, the rest V
-  static constexpr int NTB = (BC / 4) * (D / 8);       // 4 keys x 8 features blocks of K^T
   static_assert((2 * KDMA) % WAVES == 0 && KDMA % (WAVES / 2) == 0, "DMA split over the waves");
-  static_assert(NTB <= THREADS, "one K^T block per thread at most");
   static_assert(NC == 8 || NC >= 16, "swizzle assumes 8 or >= 16 chunks per row");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
   static constexpr int k_off(int st) { return st * STAGE; }
   static constexpr int v_off(int st) { return st * STAGE + KST; }
-  static constexpr int t_off(int st) { return st * STAGE + 2 * KST; }
 };
 
-// Chunk swizzle of row r of a K/V tile: with 16 or more chunks per row the 16
-// rows a half-wave reads land on 16 distinct 16-byte bank groups; with 8 chunks
-// (128-byte rows, two per 256-byte bank cycle) rows pair up by r >> 1.
+// Chunk swizzle of row r of a K/V tile, for two kinds of reads.  Row reads (16
+// lanes = 16 consecutive rows, one 16-byte chunk each) need the swizzle to be a
+// permutation over any 16 rows (for 128-byte rows, two per 256-byte bank cycle:
+// over the row pairs).  Transposing reads (a half-wave = 4 consecutive rows x 4
+// chunks, 8 bytes per lane) need the four rows to spread a chunk group over all
+// bank groups: the row's position among the four moves chunk bits 2-3 (for
+// 128-byte rows, the odd row pair flips bit 2).  The swizzle changes chunk bits
+// >= 2 only through the row, so a 32-feature block's offset is a XOR with
+// (db << 6).
 template <int NC>
-__device__ __forceinline__ int dq_swz(int r) { return NC >= 16 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int dq_swz(int r) {
+  if constexpr (NC == 8) {
+    const int u = (r >> 1) & 7;
+    return u ^ ((u & 1) << 2);
+  } else {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  }
+}
 
 // Block-sparse dQ sweep: the workgroup's 256 queries span two 128-query mask
 // rows.  Both rows go into LDS bitmaps (bit c = key block c visible); the
@@ -906,30 +916,19 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   const int swz_l = dq_swz<L::NC>(lq);
   const int kbase_lane = lq * D * 2 + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
 
-  // ---- K^T: HBM -> registers -> LDS transposed (4 keys x 8 features per thread)
-  const bool t_loader = tid < L::NTB;
-  const int kq = tid % (BC / 4), dg = tid / (BC / 4);
-  const int kq3 = kq & 3;
-  const int tpos = 16 * (kq >> 2) + 4 * (kq3 == 1 ? 2 : (kq3 == 2 ? 1 : kq3));
-  u32x4 tst[4];
-  auto t_load = [&](int k0) {
-    if (t_loader) {
+  // ---- K^T operand (A of dQ^T += K^T dS^T): lane l, row feature 32 db + l % 32,
+  // elements = keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3 of key block kb.
+  // Each half comes from one transposing read in which lane 16g + 4e + j
+  // addresses key row 4(g/2) + e (+ 8 for the second half) and features
+  // 16(g%2) + 4j .. +3; tb[sec] is that offset for kb = t = db = 0.
+  const int tg = lane >> 4, ti = lane & 15;
+  int tb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tst[i] = bload16(rk, ((unsigned)(k0 + 4 * kq + i) * D + dg * 8) * 2u);
-    }
-  };
-  auto t_store = [&](int st) {
-    if (t_loader) {
-      char* base = smem + L::t_off(st) + (dg * 8 * L::TSTR + tpos) * 2;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x2 even = {lo_lo(tst[0][w], tst[1][w]), lo_lo(tst[2][w], tst[3][w])};
-        const u32x2 odd = {hi_hi(tst[0][w], tst[1][w]), hi_hi(tst[2][w], tst[3][w])};
-        st8(base + (2 * w) * L::TSTR * 2, even);
-        st8(base + (2 * w + 1) * L::TSTR * 2, odd);
-      }
-    }
-  };
+  for (int sec = 0; sec < 2; ++sec) {
+    const int row = 8 * sec + 4 * (tg >> 1) + (ti >> 2);
+    const int c = 2 * (tg & 1) + ((ti & 3) >> 1);
+    tb[sec] = row * L::RB + ((c ^ dq_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
+  }
 
   f32x16 dq[L::NDB];
 #pragma unroll
@@ -984,8 +983,6 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
   const int j0 = next_tile(jfirst);
   kv_dma(first_row(j0), 0);
-  t_load(first_row(j0));
-  t_store(0);
   wait_vmem_all();
   __syncthreads();
 
@@ -994,7 +991,6 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     // the mask test comes before the loads of block jn: a branch between those
     // loads and the reads of stage ST would make the compiler wait for the loads
     const bool sees = wave_sees(j);
-    t_load(first_row(jn));
     kv_dma(first_row(jn), ST ^ 1);
     const int kt0 = j * BC;
     const bool in_band = BAND == 0 || (kt0 <= wb_hi && kt0 + BC - 1 >= wb_lo);
@@ -1042,21 +1038,23 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
           sf[t] = as_bf16x8(w);
         }
         // dQ^T += K_j^T dS^T: lane = query column, register = feature row
-        const char* ts = smem + L::t_off(ST);
+        const char* ks = smem + L::k_off(ST) + kb * 32 * L::RB;
         bf16x8 ta[2][L::NDB];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int db = 0; db < L::NDB; ++db)
-            ta[t][db] = as_bf16x8(ld16(ts + ((db * 32 + lq) * L::TSTR + kb * 32 + 16 * t + 8 * hf) * 2));
+          for (int db = 0; db < L::NDB; ++db) {
+            const u32x2 lo = ld8_tr(ks + 16 * t * L::RB + (tb[0] ^ (db << 6)));
+            const u32x2 hi = ld8_tr(ks + 16 * t * L::RB + (tb[1] ^ (db << 6)));
+            ta[t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < L::NDB; ++db) dq[db] = mfma32(ta[t][db], sf[t], dq[db]);
-        if constexpr (2 * L::NDB >= 6) sched_reads_ahead<2 * L::NDB>();
+        if constexpr (2 * L::NDB >= 6) sched_reads_ahead<2 * L::NDB, 4 * L::NDB>();
       }
     }
-    t_store(ST ^ 1);
     wait_vmem_all();
     __syncthreads();
   };
