@@ -450,7 +450,10 @@ __global__ __launch_bounds__(256) void row_terms_kernel(const uint16_t* __restri
 // One barrier per phase orders everything: the row-major stages and the
 // fragment buffers alternate between two slots, the transposed Q/dO tiles
 // between three (the gradient waves read tile i-1's while writing tile i+1's);
-// the loops are unrolled so that every slot is a constant offset.
+// the loops are unrolled so that every slot is a constant offset.  The barrier
+// is a bare s_barrier after the wave's own LDS writes have completed: a fence
+// would also wait for the prefetches (lse and D of the next tile, Q and dO two
+// tiles ahead) that are meant to stay in flight across it.
 // Rows past Tq and keys past Tk need no masking: their Q/dO or K/V rows read
 // as zeros, so they add nothing to the gradients that are stored.
 // ---------------------------------------------------------------------------
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     f32x16 lt0, dt0, lt1, dt1;
     int tc = next_tile(it0);                      // the tile of the next score step
     terms_load(tc, lt0, dt0);
-    __syncthreads();
+    barrier_keep_vmem();
 
     // tile t in stage ST (the step's parity in the sweep); tn is the tile after it
     auto score_step = [&](int t, int tn, auto stage, const f32x16& lt, const f32x16& dt, f32x16& lt_n,
@@ -618,7 +621,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         st16(fb + t * 1024, a);
         st16(fb + (2 + t) * 1024, b);
       }
-      __syncthreads();
+      // the fragments are complete; lse and D of the next tile stay in flight
+      wait_lds_all();
+      barrier_keep_vmem();
     };
     for (int s = 0; s < n; s += 2) {
       int tn = next_tile(tc + 1);
@@ -721,7 +726,8 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         tg = next_tile(tg + 1);
       }
     }
-    __syncthreads();
+    wait_lds_all();
+    barrier_keep_vmem();
     // phase p: gradients of sweep step p-1, stage step p+1, fetch step p+2.
     // m2 = p % 2 and m3 = p % 3 (wave-uniform counters) pick the slots.
     int m2 = 0, m3 = 0;
@@ -734,7 +740,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         gload(tg);
         tg = next_tile(tg + 1);
       }
-      __syncthreads();
+      // the staged tile is in LDS; the fetch of tile p+2 stays in flight
+      wait_lds_all();
+      barrier_keep_vmem();
       m2 ^= 1;
       m3 = up3;
     }
@@ -806,8 +814,7 @@ struct DqLayout {
   static_assert((2 * KDMA) % WAVES == 0 && KDMA % (WAVES / 2) == 0, "DMA split over the waves");
   static_assert(NC == 8 || NC >= 16, "swizzle assumes 8 or >= 16 chunks per row");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
-  static constexpr int k_off(int st) { return st * STAGE; }
-  static constexpr int v_off(int st) { return st * STAGE + KST; }
+  static constexpr int K_OFF = 0, V_OFF = KST;        // within a stage
 };
 
 // Chunk swizzle of row r of a K/V tile, for two kinds of reads.  Row reads (16
@@ -845,7 +852,11 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   constexpr int BC = L::BC;
   static_assert(kMaskBlock % BC == 0 && L::BR % kMaskBlock == 0 && L::BR <= 2 * kMaskBlock,
                 "one or two mask rows, whole tiles per mask block");
-  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+  // One LDS array per pipeline stage (distinct alias scopes: reads of one stage
+  // need not wait for the DMA in flight into the other).
+  __shared__ __attribute__((aligned(1024))) char stage0[L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[L::STAGE];
+  auto stage_ptr = [&](int st) -> char* { return st == 0 ? stage0 : stage1; };
 
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
@@ -909,7 +920,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
       const int row = s / L::NC, cp = s % L::NC;
       const unsigned off = ((unsigned)(k0 + row) * D + (cp ^ dq_swz<L::NC>(row)) * 8) * 2u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rkv, (__attribute__((address_space(3))) void*)(smem + L::k_off(st) + g * 1024), 16, off, 0, 0, 0);
+          rkv, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, off, 0, 0, 0);
     }
   };
   // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
@@ -1007,8 +1018,8 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 #pragma unroll
         for (int ds = 0; ds < L::NDS; ++ds) {
           const int off = kb * 32 * D * 2 + (kbase_lane ^ (ds << 5));
-          ka[ds] = as_bf16x8(ld16(smem + L::k_off(ST) + off));
-          va[ds] = as_bf16x8(ld16(smem + L::v_off(ST) + off));
+          ka[ds] = as_bf16x8(ld16(stage_ptr(ST) + L::K_OFF + off));
+          va[ds] = as_bf16x8(ld16(stage_ptr(ST) + L::V_OFF + off));
         }
 #pragma unroll
         for (int ds = 0; ds < L::NDS; ++ds) {
@@ -1038,7 +1049,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
           sf[t] = as_bf16x8(w);
         }
         // dQ^T += K_j^T dS^T: lane = query column, register = feature row
-        const char* ks = smem + L::k_off(ST) + kb * 32 * L::RB;
+        const char* ks = stage_ptr(ST) + L::K_OFF + kb * 32 * L::RB;
         bf16x8 ta[2][L::NDB];
 #pragma unroll
         for (int t = 0; t < 2; ++t)

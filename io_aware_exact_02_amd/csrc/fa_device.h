@@ -88,6 +88,25 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // already consumed its loads, it tells the compiler's wait-count tracking that
 // nothing is outstanding at the back edge.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt lgkmcnt(0): this wave's LDS (and scalar) accesses have completed.
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without a memory fence.  __syncthreads() is a release fence
+// plus s_barrier, and the fence waits for every vector-memory load still in
+// flight -- LDS DMA included -- which would drain a prefetch meant to stay in
+// flight across the barrier.  This is the bare s_barrier; the "memory" clobber
+// keeps the compiler from moving memory accesses across it.  The caller makes
+// what others must see complete first: its LDS writes (wait_lds_all) and the
+// DMA loads that must have landed (wait_vmem_le / wait_vmem_all).
+__device__ __forceinline__ void barrier_keep_vmem() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N), N <= 15: at most the N vector memory loads issued last are
+// still outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N <= 15, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Low / high bf16 halves of two words, packed (word a -> low half, word b -> high
 // half); one v_perm_b32 each (selector bytes 0-3 pick from a, 4-7 from b).

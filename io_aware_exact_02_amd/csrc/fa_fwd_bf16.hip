@@ -67,8 +67,7 @@ struct FwdLayout {
   static constexpr int KDMA_W = KDMA / kWaves;       // ... per wave
   static_assert(KDMA % kWaves == 0, "K tile must split evenly over the waves");
   static_assert(NC == 8 || NC >= 16, "swizzle assumes 8 or >= 16 chunks per row");
-  static constexpr int k_off(int st) { return st * KST; }
-  static constexpr int v_off(int st) { return (2 + st) * KST; }
+  static constexpr int K_OFF = 0, V_OFF = KST;      // within a stage
 };
 
 // Chunk swizzle of K row r: with 16 or more chunks per row the 16 rows a
@@ -97,7 +96,15 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      const int* __restrict__ cu, int nd, int bcausal) {
   using L = FwdLayout<D>;
   constexpr int BC = L::BC;
-  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+  // One LDS array per pipeline stage: accesses to distinct arrays carry distinct
+  // alias scopes, which lets the compiler see that reads of one stage do not
+  // touch the DMA in flight into the other (it would wait for the DMA otherwise).
+  __shared__ __attribute__((aligned(1024))) char stage0[L::BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) char stage1[L::BYTES / 2];
+  auto stage_ptr = [&](auto st) -> char* {
+    if constexpr (decltype(st)::value == 0) return stage0;
+    else return stage1;
+  };
 
   // Workgroup -> (head, query block).  Consecutive workgroup ids go to
   // different XCDs round-robin; remapping gives each XCD a contiguous range of
@@ -145,7 +152,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 
   // ---- K and V: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
-  auto k_dma = [&](int k0, int kst_off) {
+  auto k_dma = [&](int k0, char* kst) {
 #pragma unroll
     for (int i = 0; i < L::KDMA_W; ++i) {
       const int g = wave * L::KDMA_W + i;
@@ -154,10 +161,10 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       const int src = cp ^ kswz<L::NC>(row);
       const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(smem + kst_off + g * 1024), 16, off, 0, 0, 0);
+          rk, (__attribute__((address_space(3))) void*)(kst + g * 1024), 16, off, 0, 0, 0);
     }
   };
-  auto v_dma = [&](int k0, int vst_off) {
+  auto v_dma = [&](int k0, char* vst) {
 #pragma unroll
     for (int i = 0; i < L::KDMA_W; ++i) {
       const int g = wave * L::KDMA_W + i;
@@ -166,7 +173,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       const int src = cp ^ vswz<L::NC>(row);
       const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)(smem + vst_off + g * 1024), 16, off, 0, 0, 0);
+          rv, (__attribute__((address_space(3))) void*)(vst + g * 1024), 16, off, 0, 0, 0);
     }
   };
   // Per-lane K read offset (bytes, relative to a stage and a 32-key block) for
@@ -194,7 +201,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   float l_part = 0.f;        // this lane's share of the sum of the weights
   float lr_part = 0.f;       // ... and of the bf16-rounded weights
 
-  auto s_product = [&](f32x16 (&s)[L::NKB], int kst_off) {
+  auto s_product = [&](f32x16 (&s)[L::NKB], const char* kst) {
 #pragma unroll
     for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
@@ -204,7 +211,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int ds = 0; ds < L::NDS; ++ds)
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb)
-        ka[ds][kb] = as_bf16x8(ld16(smem + kst_off + kb * 32 * D * 2 + (kbase_lane ^ (ds << 5))));
+        ka[ds][kb] = as_bf16x8(ld16(kst + kb * 32 * D * 2 + (kbase_lane ^ (ds << 5))));
 #pragma unroll
     for (int ds = 0; ds < L::NDS; ++ds)
 #pragma unroll
@@ -275,18 +282,20 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // move no data, so the steps below need no branches around their loads.
   auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
   const int j0 = next_tile(jfirst);
-  k_dma(first_row(j0), L::k_off(0));
-  v_dma(first_row(j0), L::v_off(0));
+  k_dma(first_row(j0), stage_ptr(std::integral_constant<int, 0>{}) + L::K_OFF);
+  v_dma(first_row(j0), stage_ptr(std::integral_constant<int, 0>{}) + L::V_OFF);
   wait_vmem_all();
   __syncthreads();
 
   auto step = [&](int j, int jn, auto stage) {
     constexpr int ST = decltype(stage)::value;        // position of block j in the sweep, mod 2
     // the next visited block jn in flight, straight into the other LDS stage
-    k_dma(first_row(jn), L::k_off(ST ^ 1));
-    v_dma(first_row(jn), L::v_off(ST ^ 1));
+    char* const cur = stage_ptr(std::integral_constant<int, ST>{});
+    char* const nxt = stage_ptr(std::integral_constant<int, ST ^ 1>{});
+    k_dma(first_row(jn), nxt + L::K_OFF);
+    v_dma(first_row(jn), nxt + L::V_OFF);
     f32x16 s[L::NKB];
-    s_product(s, L::k_off(ST));
+    s_product(s, cur + L::K_OFF);
     mask_tile(s, j);
     // row maximum and (below) row sums as shallow trees of independent partial
     // results: long chains of dependent vector ops leave the wave stalled
@@ -343,7 +352,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
     // O~^T += V_j^T P~_j^T (independent accumulators back to back)
-    const char* vs = smem + L::v_off(ST);
+    const char* vs = cur + L::V_OFF;
     bf16x8 va[L::NKB][2][L::NDB];
 #pragma unroll
     for (int kb = 0; kb < L::NKB; ++kb)
