@@ -1027,6 +1027,16 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
           dp = mfma32(va[ds], gf[ds], dp);
         }
         sched_reads_ahead<2 * L::NDS>();
+        // K^T operands of the dQ product for k-step t = 0, read now so that their
+        // latency hides behind the softmax (all of them at once would spill)
+        const char* ks = stage_ptr(ST) + L::K_OFF + kb * 32 * L::RB;
+        bf16x8 ta[2][L::NDB];
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) {
+          const u32x2 lo = ld8_tr(ks + (tb[0] ^ (db << 6)));
+          const u32x2 hi = ld8_tr(ks + (tb[1] ^ (db << 6)));
+          ta[0][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, lnq));
@@ -1048,22 +1058,18 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
           }
           sf[t] = as_bf16x8(w);
         }
-        // dQ^T += K_j^T dS^T: lane = query column, register = feature row
-        const char* ks = stage_ptr(ST) + L::K_OFF + kb * 32 * L::RB;
-        bf16x8 ta[2][L::NDB];
+        // dQ^T += K_j^T dS^T: lane = query column, register = feature row (the
+        // operands of k-step t = 1 are read here)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int db = 0; db < L::NDB; ++db) {
-            const u32x2 lo = ld8_tr(ks + 16 * t * L::RB + (tb[0] ^ (db << 6)));
-            const u32x2 hi = ld8_tr(ks + 16 * t * L::RB + (tb[1] ^ (db << 6)));
-            ta[t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          }
+        for (int db = 0; db < L::NDB; ++db) {
+          const u32x2 lo = ld8_tr(ks + 16 * L::RB + (tb[0] ^ (db << 6)));
+          const u32x2 hi = ld8_tr(ks + 16 * L::RB + (tb[1] ^ (db << 6)));
+          ta[1][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < L::NDB; ++db) dq[db] = mfma32(ta[t][db], sf[t], dq[db]);
-        if constexpr (2 * L::NDB >= 6) sched_reads_ahead<2 * L::NDB, 4 * L::NDB>();
       }
     }
     wait_vmem_all();

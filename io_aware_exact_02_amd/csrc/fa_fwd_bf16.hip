@@ -296,6 +296,19 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     v_dma(first_row(jn), nxt + L::V_OFF);
     f32x16 s[L::NKB];
     s_product(s, cur + L::K_OFF);
+    // V^T operands of the PV product, read now so that their latency hides behind the softmax
+    const char* vs = cur + L::V_OFF;
+    bf16x8 va[L::NKB][2][L::NDB];
+#pragma unroll
+    for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) {
+          const char* p = vs + (32 * kb + 16 * t) * L::RB + (vlane ^ (db << 6));
+          const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
+          va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
     mask_tile(s, j);
     // row maximum and (below) row sums as shallow trees of independent partial
     // results: long chains of dependent vector ops leave the wave stalled
@@ -352,25 +365,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
     // O~^T += V_j^T P~_j^T (independent accumulators back to back)
-    const char* vs = cur + L::V_OFF;
-    bf16x8 va[L::NKB][2][L::NDB];
-#pragma unroll
-    for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db) {
-          const char* p = vs + (32 * kb + 16 * t) * L::RB + (vlane ^ (db << 6));
-          const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
-          va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        }
 #pragma unroll
     for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
-    sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
     wait_vmem_all();
     __syncthreads();
   };
