@@ -296,19 +296,24 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     v_dma(first_row(jn), nxt + L::V_OFF);
     f32x16 s[L::NKB];
     s_product(s, cur + L::K_OFF);
-    // V^T operands of the PV product, read now so that their latency hides behind the softmax
+    // V^T operands of the PV product.  For d <= 128 they are read here, so that
+    // their latency hides behind the softmax; at d = 256 (one wave per SIMD, all
+    // registers in use) holding them that long costs more than it hides.
     const char* vs = cur + L::V_OFF;
     bf16x8 va[L::NKB][2][L::NDB];
+    auto read_va = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < L::NKB; ++kb)
+      for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int db = 0; db < L::NDB; ++db) {
-          const char* p = vs + (32 * kb + 16 * t) * L::RB + (vlane ^ (db << 6));
-          const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
-          va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        }
+          for (int db = 0; db < L::NDB; ++db) {
+            const char* p = vs + (32 * kb + 16 * t) * L::RB + (vlane ^ (db << 6));
+            const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
+            va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          }
+    };
+    if constexpr (D <= 128) read_va();
     mask_tile(s, j);
     // row maximum and (below) row sums as shallow trees of independent partial
     // results: long chains of dependent vector ops leave the wave stalled
@@ -365,12 +370,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
     // O~^T += V_j^T P~_j^T (independent accumulators back to back)
+    if constexpr (D > 128) read_va();
 #pragma unroll
     for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
+    if constexpr (D > 128) sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
     wait_vmem_all();
     __syncthreads();
   };
