@@ -29,7 +29,11 @@
  * every launch was accepted, and faults surface at the caller's next
  * synchronisation.  All argument checks run before any device work; on an
  * error nothing is launched and no output is touched.  NaN or Inf inputs are
- * not checked: they propagate to the outputs.
+ * not checked: they propagate to the outputs that depend on them (a NaN in a
+ * query row reaches that row only; a NaN in a key's K row reaches only the rows
+ * that see the key, since masked scores are -inf whatever their value).  A NaN
+ * in a V row can also reach rows that do not see that key when its tile is
+ * computed for them (a zero weight times NaN is NaN).
  */
 #ifndef FA_H
 #define FA_H

@@ -1,0 +1,57 @@
+"""NaN inputs through the C ABI: they are not checked and propagate, but only to the
+outputs that depend on them (rows are independent in the forward; a causal mask keeps
+a key's NaN from the rows before it).  The other rows must still match the float64
+oracle, which follows the same rule: a masked score is -inf whatever its value."""
+import math
+
+import numpy as np
+import pytest
+
+import io_aware_exact_02_amd as fa
+from io_aware_exact_02_amd import inputs as I
+from oracle import naive
+from tests.gpu_util import TOL_LSE, TOL_O, maxabs, to_dev, to_f64, torch
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_nan_in_one_query_row_stays_in_that_row(d):
+    B, H, T = 1, 2, 300
+    r = 137
+    raw = I.draw(B, H, T, T, d, "bf16", 9700 + d)
+    raw["q"][0, 1, r, 5] = NAN_BF16
+    q, k, v = (to_dev(raw[n], "bf16") for n in ("q", "k", "v"))
+    O, lse = fa.forward(q, k, v, causal=False)
+    torch().cuda.synchronize()
+    O, lse = to_f64(O), to_f64(lse)
+    assert np.isnan(O[0, 1, r]).all() and np.isnan(lse[0, 1, r])
+    keep = np.ones(T, bool)
+    keep[r] = False
+    assert np.isfinite(O[0, 1, keep]).all() and np.isfinite(O[0, 0]).all()
+    f = {n: I.as_f64(raw[n], "bf16") for n in ("q", "k", "v")}
+    Or, Lr = naive.forward(f["q"], f["k"], f["v"], 1 / math.sqrt(d), False)
+    assert maxabs(O[0, 1, keep], Or[0, 1, keep]) <= TOL_O["bf16"]
+    assert maxabs(O[0, 0], Or[0, 0]) <= TOL_O["bf16"]
+    assert maxabs(lse[0, 1, keep], Lr[0, 1, keep]) <= TOL_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("l", [0, 70, 299])
+def test_nan_in_a_key_reaches_only_the_rows_that_see_it(d, l):
+    B, H, T = 1, 1, 300
+    raw = I.draw(B, H, T, T, d, "bf16", 9800 + d + l)
+    raw["k"][0, 0, l, 3] = NAN_BF16
+    q, k, v = (to_dev(raw[n], "bf16") for n in ("q", "k", "v"))
+    O, lse = fa.forward(q, k, v, causal=True)
+    torch().cuda.synchronize()
+    O, lse = to_f64(O), to_f64(lse)
+    assert np.isnan(O[0, 0, l:]).all() and np.isnan(lse[0, 0, l:]).all()
+    if l > 0:
+        f = {n: I.as_f64(raw[n], "bf16") for n in ("q", "k", "v")}
+        Or, Lr = naive.forward(f["q"], f["k"], f["v"], 1 / math.sqrt(d), True)
+        assert np.isfinite(O[0, 0, :l]).all()
+        assert maxabs(O[0, 0, :l], Or[0, 0, :l]) <= TOL_O["bf16"]
+        assert maxabs(lse[0, 0, :l], Lr[0, 0, :l]) <= TOL_LSE
