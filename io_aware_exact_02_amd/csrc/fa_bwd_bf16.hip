@@ -163,7 +163,7 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
   const int bh = lin / nkb;
-  const int kblk = CAUSAL ? nkb - 1 - (lin % nkb) : (lin % nkb);   // causal: longest sweeps first
+  const int kblk = lin % nkb;   // causal: key block 0 has the longest sweep, so it goes first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
   const int bh = lin / nkb;
-  const int kblk = CAUSAL ? nkb - 1 - (lin % nkb) : (lin % nkb);   // causal: longest sweeps first
+  const int kblk = lin % nkb;   // causal: key block 0 has the longest sweep, so it goes first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
