@@ -346,6 +346,11 @@ def main(argv=None):
     names = ["fwd", "bwd_pre", "bwd_main", "bwd_post"]
     dur = {n: sum(events[s][i].elapsed_time(events[s][i + 1]) for s in range(a.steps)) / a.steps
            for i, n in enumerate(names)}
+    # per-step times from the events on the launch stream: median and spread
+    per_step = sorted(events[s][0].elapsed_time(events[s][4]) for s in range(a.steps))
+    step_stats = {"median_ms": round(per_step[len(per_step) // 2] if len(per_step) % 2 else
+                                     0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2]), 4),
+                  "min_ms": round(per_step[0], 4), "max_ms": round(per_step[-1], 4)}
     f_fwd, f_bwd = w.flops_fwd(), w.flops_bwd()
     if bmask_np is not None:                    # kept pairs only: 4 d per visible (query, key) pair
         f_fwd = 4.0 * d * B * float(mask_pairs(bmask_np, Tq, Tk, w.causal).sum())
@@ -388,6 +393,7 @@ def main(argv=None):
         "config": {"workload": f"{w.name}_fwd_bwd", "B": B, "H": H, "Tq": Tq, "Tk": Tk, "d": d,
                    "causal": w.causal, "pass": "forward+backward"},
         "pct_of_peak": round(100 * value / peak, 2),
+        "step_events": step_stats,
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }
     if w.window is not None:

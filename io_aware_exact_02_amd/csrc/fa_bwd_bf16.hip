@@ -716,7 +716,8 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       sched_reads_ahead<4 * L::NDB, 4 * L::NDB + 4>();
     };
 
-    int tg = next_tile(it0);                         // the tile of the next fetch
+    int tgr = next_tile(it0);                        // the tile of the next gradient step
+    int tg = tgr;                                    // the tile of the next fetch
     if (n > 0) {
       gload(tg);
       lstore(0, 0);
@@ -734,7 +735,11 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     for (int p = 0; p < n; ++p) {
       const int up3 = m3 == 2 ? 0 : m3 + 1;          // (p + 1) % 3
       const int dn3 = m3 == 0 ? 2 : m3 - 1;          // (p - 1) % 3
-      if (p >= 1) grad_step(m2 ^ 1, dn3);
+      if (p >= 1) {
+        // causal: a query tile wholly before this wave's keys has all-zero fragments
+        if (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0) grad_step(m2 ^ 1, dn3);
+        tgr = next_tile(tgr + 1);
+      }
       if (p + 1 < n) lstore(m2 ^ 1, up3);
       if (p + 2 < n) {
         gload(tg);
@@ -747,7 +752,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       m3 = up3;
     }
     // the last tile's gradients: its slots are ((n-1) % 2, (n-1) % 3)
-    if (n > 0) grad_step(m2 ^ 1, m3 == 0 ? 2 : m3 - 1);
+    if (n > 0 && (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0)) grad_step(m2 ^ 1, m3 == 0 ? 2 : m3 - 1);
 
     // dK_j = scale * dS^T Q and dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
     const unsigned gsz = grad_f32 ? 4u : 2u;
