@@ -254,8 +254,8 @@ def main(argv=None):
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(heads shard across GPUs with no exchange; see the design notes). Use --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange). Use --gpus 1.",
               file=sys.stderr)
         return 2
     import torch
