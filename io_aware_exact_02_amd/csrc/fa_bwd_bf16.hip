@@ -497,282 +497,299 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   using L = KvLayout<D>;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
+  // Plain causal at d = 128: workgroup p of a head runs key block p, then key
+  // block nkb-1-p, so every workgroup sweeps about the same number of query
+  // tiles (uneven workgroups leave CUs waiting on the dispatcher).  At d = 64
+  // the loop over two blocks compiles to a slower sweep (2-5% measured) than
+  // the dispatch gaps it removes.  Otherwise one block per workgroup; causal
+  // key block 0 has the longest sweep and goes first.
+  constexpr bool PAIRED = CAUSAL && !MASKED && BAND == 0 && D == 128;
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
-  const int bh = lin / nkb;
-  const int kblk = lin % nkb;   // causal: key block 0 has the longest sweep, so it goes first
+  const int npb = PAIRED ? (nkb + 1) / 2 : nkb;     // workgroups per head
+  const int bh = lin / npb;
+  const int pidx = lin % npb;
+  const int npass = (PAIRED && 2 * pidx + 1 < nkb) ? 2 : 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int wq = wave & 3;                      // key slice (score wave w and gradient wave 4+w)
   const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
-  const int k0 = kblk * kBKC;
-  const int kw0 = k0 + wq * kKeysPerWave;
-  const int mykey = kw0 + l32;
-
-  const int nqt = (Tq + kBQ - 1) / kBQ;
-  // BAND: the queries that see this block's keys, and those that see every key
-  // of this wave (a tile between them needs no element mask), from the key side
-  const Band<BAND> band{wl, wr, cu, nd, bcausal};
-  int w_qlo = 0, w_qhi = 0, my_qlo = 0, my_qhi = 0;   // and this lane's key: my_qlo .. my_qhi
-  if constexpr (BAND != 0) {
-    w_qlo = band.qlo(kw0 + kKeysPerWave - 1);
-    w_qhi = band.qhi(kw0);
-    band.queries(mykey, my_qlo, my_qhi);
-  }
-  const int it0 = BAND != 0 ? min(max(0, band.qlo(k0)) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
-  // tile t covers query rows t kBQ ..; a tile past the sweep reads row Tq (zeros)
-  auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
-
-  // visible query tiles: all from it0 on, or (masked) those whose block keeps this key block
-  KeyBlockTiles<MASKED, BAND != 0> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
-  if constexpr (BAND != 0) {
-    const int qh = band.qhi(min(k0 + kBKC, Tk) - 1);
-    tiles.nqe = qh < 0 ? 0 : min(nqt, qh / kBQ + 1);
-  }
-  const int n = tiles.count();                  // query tiles in the sweep
-  auto next_tile = [&](int t) { return tiles.next(t); };
-
-  if (wave < 4) {
-    // ============================ score waves ============================
-    const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
-    const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
-    const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
-    const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
-    bf16x8 kf[L::NDS], vf[L::NDS];
-#pragma unroll
-    for (int ds = 0; ds < L::NDS; ++ds) {
-      const unsigned off = ((unsigned)mykey * D + ds * 16 + 8 * hf) * 2u;
-      kf[ds] = as_bf16x8(bload16(rk, off));
-      vf[ds] = as_bf16x8(bload16(rv, off));
-    }
-    // -lse log2e and -D of the tile's queries in the accumulator order:
-    // register r <-> query 8(r/4) + 4hf + r%4 (all lanes of a half alike)
-    auto terms_load = [&](int t, f32x16& lt, f32x16& dt) {
-      const int r0 = tile_row(t);
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const unsigned off = (unsigned)(r0 + 8 * g4 + 4 * hf) * 4u;
-        const f32x4 a = __builtin_bit_cast(f32x4, bload16(rl, off));
-        const f32x4 b = __builtin_bit_cast(f32x4, bload16(rd, off));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lt[4 * g4 + e] = a[e];
-          dt[4 * g4 + e] = b[e];
-        }
-      }
-    };
-    // this lane's row-major operand reads: query row l32, chunk 2 ds + hf (layout in KvLayout)
-    const int n_lane = (l32 & 3) * L::NB + (8 * hf + (l32 >> 2)) * 16;
-    f32x16 lt0, dt0, lt1, dt1;
-    int tc = next_tile(it0);                      // the tile of the next score step
-    terms_load(tc, lt0, dt0);
-    barrier_keep_vmem();
-
-    // tile t in stage ST (the step's parity in the sweep); tn is the tile after it
-    auto score_step = [&](int t, int tn, auto stage, const f32x16& lt, const f32x16& dt, f32x16& lt_n,
-                          f32x16& dt_n) {
-      constexpr int ST = decltype(stage)::value;
-      terms_load(tn, lt_n, dt_n);
-      const int r0 = t * kBQ;
-      const char* sb_ = smem + ST * L::STAGE;
-      // S = Q_i K_j^T and dP - D = dO_i V_j^T - D_i: lane = key, register r = query 8(r/4)+4hf+r%4
-      f32x16 sacc, dp = dt;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-      bf16x8 qa[L::NDS], ga[L::NDS];
-#pragma unroll
-      for (int ds = 0; ds < L::NDS; ++ds) {
-        qa[ds] = as_bf16x8(ld16(sb_ + L::Q_N + n_lane + ds * 256));
-        ga[ds] = as_bf16x8(ld16(sb_ + L::G_N + n_lane + ds * 256));
-      }
-#pragma unroll
-      for (int ds = 0; ds < L::NDS; ++ds) {
-        sacc = mfma32(qa[ds], kf[ds], sacc);
-        dp = mfma32(ga[ds], vf[ds], dp);
-      }
-      sched_reads_ahead<2 * L::NDS>();
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sacc[r], cl2e, lt[r]));
-      if (CAUSAL && r0 < kw0 + kKeysPerWave - 1) {     // the tile crosses this wave's diagonal
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
-      }
-      if (BAND != 0 && !(r0 >= w_qlo && r0 + kBQ - 1 <= w_qhi)) {   // crosses a band edge
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = r0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (qr < my_qlo || qr > my_qhi) p[r] = 0.f;
-        }
-      }
-      // fragments for the gradient wave: [P^T t=0, P^T t=1, dS^T t=0, dS^T t=1], 1 KiB each
-      char* fb = smem + L::F_OFF + ST * L::F_BYTES + wq * L::F_WAVE + lane * 16;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 a, b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * t + 2 * e;
-          a[e] = pack_bf16(p[r], p[r + 1]);
-          b[e] = pack_bf16(p[r] * dp[r], p[r + 1] * dp[r + 1]);
-        }
-        st16(fb + t * 1024, a);
-        st16(fb + (2 + t) * 1024, b);
-      }
-      // the fragments are complete; lse and D of the next tile stay in flight
+  for (int pass = 0; pass < npass; ++pass) {
+    const int kblk = pass == 0 ? pidx : nkb - 1 - pidx;
+    if (pass > 0) {
+      // the gradient waves' last step read the previous block's LDS slots
       wait_lds_all();
       barrier_keep_vmem();
-    };
-    for (int s = 0; s < n; s += 2) {
-      int tn = next_tile(tc + 1);
-      score_step(tc, tn, std::integral_constant<int, 0>{}, lt0, dt0, lt1, dt1);
-      tc = tn;
-      if (s + 1 < n) {
-        tn = next_tile(tc + 1);
-        score_step(tc, tn, std::integral_constant<int, 1>{}, lt1, dt1, lt0, dt0);
-        tc = tn;
-      }
     }
-  } else {
-    // =========================== gradient waves ==========================
-    const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
-    const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
+    const int k0 = kblk * kBKC;
+    const int kw0 = k0 + wq * kKeysPerWave;
+    const int mykey = kw0 + l32;
 
-    // Staging: WPT waves per tensor (Q, then dO); lane sidx = 8 fg + qa holds 4
-    // consecutive query rows (quad qa) x 8 features (group fg).  A tile index
-    // past the sweep maps to row Tq, whose loads return zeros.
-    const bool stager = wave >= L::SW0;
-    const bool is_g = wave >= L::SW0 + L::WPT;
-    const int sidx = ((wave - L::SW0) % L::WPT) * 64 + lane;
-    const int qa = sidx & 7, fg = sidx >> 3;
-    const rsrc_t rsrc = is_g ? rg : rq;
-    // transposed position of the quad: the middle quads of each 16 queries are
-    // swapped, matching the query order of a fragment's MFMA k-slots
-    const int tpos = 16 * (qa >> 2) + 4 * (((qa & 1) << 1) | ((qa >> 1) & 1));
-    const int n_off = (is_g ? L::G_N : L::Q_N) + sidx * 16;     // row 4 qa + i, chunk fg: i NB + 16 sidx
-    const int t_off = (is_g ? L::GT_OFF : L::QT_OFF) + ((fg * 8) * L::TSTR + tpos) * 2;
-    u32x4 stg[4];
-    auto gload = [&](int t) {
-      if (stager) {
+    const int nqt = (Tq + kBQ - 1) / kBQ;
+    // BAND: the queries that see this block's keys, and those that see every key
+    // of this wave (a tile between them needs no element mask), from the key side
+    const Band<BAND> band{wl, wr, cu, nd, bcausal};
+    int w_qlo = 0, w_qhi = 0, my_qlo = 0, my_qhi = 0;   // and this lane's key: my_qlo .. my_qhi
+    if constexpr (BAND != 0) {
+      w_qlo = band.qlo(kw0 + kKeysPerWave - 1);
+      w_qhi = band.qhi(kw0);
+      band.queries(mykey, my_qlo, my_qhi);
+    }
+    const int it0 = BAND != 0 ? min(max(0, band.qlo(k0)) / kBQ, nqt) : CAUSAL ? min(k0 / kBQ, nqt) : 0;
+    // tile t covers query rows t kBQ ..; a tile past the sweep reads row Tq (zeros)
+    auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
+
+    // visible query tiles: all from it0 on, or (masked) those whose block keeps this key block
+    KeyBlockTiles<MASKED, BAND != 0> tiles(bmask, (long long)(bh % H) * mask_hstride, kblk, nmk, Tq, it0, lane);
+    if constexpr (BAND != 0) {
+      const int qh = band.qhi(min(k0 + kBKC, Tk) - 1);
+      tiles.nqe = qh < 0 ? 0 : min(nqt, qh / kBQ + 1);
+    }
+    const int n = tiles.count();                  // query tiles in the sweep
+    auto next_tile = [&](int t) { return tiles.next(t); };
+
+    if (wave < 4) {
+      // ============================ score waves ============================
+      const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
+      const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
+      const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
+      const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
+      bf16x8 kf[L::NDS], vf[L::NDS];
+#pragma unroll
+      for (int ds = 0; ds < L::NDS; ++ds) {
+        const unsigned off = ((unsigned)mykey * D + ds * 16 + 8 * hf) * 2u;
+        kf[ds] = as_bf16x8(bload16(rk, off));
+        vf[ds] = as_bf16x8(bload16(rv, off));
+      }
+      // -lse log2e and -D of the tile's queries in the accumulator order:
+      // register r <-> query 8(r/4) + 4hf + r%4 (all lanes of a half alike)
+      auto terms_load = [&](int t, f32x16& lt, f32x16& dt) {
         const int r0 = tile_row(t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) stg[i] = bload16(rsrc, ((unsigned)(r0 + 4 * qa + i) * D + fg * 8) * 2u);
-      }
-    };
-    auto lstore = [&](int slot2, int slot3) {     // slots s % 2 and s % 3 of the tile staged
-      if (stager) {
-        char* N = smem + slot2 * L::STAGE + n_off;
-        char* T = smem + slot3 * L::T_BYTES + t_off;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const unsigned off = (unsigned)(r0 + 8 * g4 + 4 * hf) * 4u;
+          const f32x4 a = __builtin_bit_cast(f32x4, bload16(rl, off));
+          const f32x4 b = __builtin_bit_cast(f32x4, bload16(rd, off));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st16(N + i * L::NB, stg[i]);
+          for (int e = 0; e < 4; ++e) {
+            lt[4 * g4 + e] = a[e];
+            dt[4 * g4 + e] = b[e];
+          }
+        }
+      };
+      // this lane's row-major operand reads: query row l32, chunk 2 ds + hf (layout in KvLayout)
+      const int n_lane = (l32 & 3) * L::NB + (8 * hf + (l32 >> 2)) * 16;
+      f32x16 lt0, dt0, lt1, dt1;
+      int tc = next_tile(it0);                      // the tile of the next score step
+      terms_load(tc, lt0, dt0);
+      barrier_keep_vmem();
+
+      // tile t in stage ST (the step's parity in the sweep); tn is the tile after it
+      auto score_step = [&](int t, int tn, auto stage, const f32x16& lt, const f32x16& dt, f32x16& lt_n,
+                            f32x16& dt_n) {
+        constexpr int ST = decltype(stage)::value;
+        terms_load(tn, lt_n, dt_n);
+        const int r0 = t * kBQ;
+        const char* sb_ = smem + ST * L::STAGE;
+        // S = Q_i K_j^T and dP - D = dO_i V_j^T - D_i: lane = key, register r = query 8(r/4)+4hf+r%4
+        f32x16 sacc, dp = dt;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const u32x2 ev = {lo_lo(stg[0][w], stg[1][w]), lo_lo(stg[2][w], stg[3][w])};
-          const u32x2 od = {hi_hi(stg[0][w], stg[1][w]), hi_hi(stg[2][w], stg[3][w])};
-          st8(T + (2 * w) * L::TSTR * 2, ev);
-          st8(T + (2 * w + 1) * L::TSTR * 2, od);
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        bf16x8 qa[L::NDS], ga[L::NDS];
+#pragma unroll
+        for (int ds = 0; ds < L::NDS; ++ds) {
+          qa[ds] = as_bf16x8(ld16(sb_ + L::Q_N + n_lane + ds * 256));
+          ga[ds] = as_bf16x8(ld16(sb_ + L::G_N + n_lane + ds * 256));
+        }
+#pragma unroll
+        for (int ds = 0; ds < L::NDS; ++ds) {
+          sacc = mfma32(qa[ds], kf[ds], sacc);
+          dp = mfma32(ga[ds], vf[ds], dp);
+        }
+        sched_reads_ahead<2 * L::NDS>();
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sacc[r], cl2e, lt[r]));
+        if (CAUSAL && r0 < kw0 + kKeysPerWave - 1) {     // the tile crosses this wave's diagonal
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (mykey > r0 + 8 * (r >> 2) + 4 * hf + (r & 3)) p[r] = 0.f;
+        }
+        if (BAND != 0 && !(r0 >= w_qlo && r0 + kBQ - 1 <= w_qhi)) {   // crosses a band edge
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qr = r0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (qr < my_qlo || qr > my_qhi) p[r] = 0.f;
+          }
+        }
+        // fragments for the gradient wave: [P^T t=0, P^T t=1, dS^T t=0, dS^T t=1], 1 KiB each
+        char* fb = smem + L::F_OFF + ST * L::F_BYTES + wq * L::F_WAVE + lane * 16;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 a, b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * t + 2 * e;
+            a[e] = pack_bf16(p[r], p[r + 1]);
+            b[e] = pack_bf16(p[r] * dp[r], p[r + 1] * dp[r + 1]);
+          }
+          st16(fb + t * 1024, a);
+          st16(fb + (2 + t) * 1024, b);
+        }
+        // the fragments are complete; lse and D of the next tile stay in flight
+        wait_lds_all();
+        barrier_keep_vmem();
+      };
+      for (int s = 0; s < n; s += 2) {
+        int tn = next_tile(tc + 1);
+        score_step(tc, tn, std::integral_constant<int, 0>{}, lt0, dt0, lt1, dt1);
+        tc = tn;
+        if (s + 1 < n) {
+          tn = next_tile(tc + 1);
+          score_step(tc, tn, std::integral_constant<int, 1>{}, lt1, dt1, lt0, dt0);
+          tc = tn;
         }
       }
-    };
+    } else {
+      // =========================== gradient waves ==========================
+      const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+      const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
 
-    f32x16 dk[L::NDB], dv[L::NDB];
+      // Staging: WPT waves per tensor (Q, then dO); lane sidx = 8 fg + qa holds 4
+      // consecutive query rows (quad qa) x 8 features (group fg).  A tile index
+      // past the sweep maps to row Tq, whose loads return zeros.
+      const bool stager = wave >= L::SW0;
+      const bool is_g = wave >= L::SW0 + L::WPT;
+      const int sidx = ((wave - L::SW0) % L::WPT) * 64 + lane;
+      const int qa = sidx & 7, fg = sidx >> 3;
+      const rsrc_t rsrc = is_g ? rg : rq;
+      // transposed position of the quad: the middle quads of each 16 queries are
+      // swapped, matching the query order of a fragment's MFMA k-slots
+      const int tpos = 16 * (qa >> 2) + 4 * (((qa & 1) << 1) | ((qa >> 1) & 1));
+      const int n_off = (is_g ? L::G_N : L::Q_N) + sidx * 16;     // row 4 qa + i, chunk fg: i NB + 16 sidx
+      const int t_off = (is_g ? L::GT_OFF : L::QT_OFF) + ((fg * 8) * L::TSTR + tpos) * 2;
+      u32x4 stg[4];
+      auto gload = [&](int t) {
+        if (stager) {
+          const int r0 = tile_row(t);
 #pragma unroll
-    for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk[db][r] = 0.f;
-        dv[db][r] = 0.f;
-      }
-    const int f_lane = L::F_OFF + wq * L::F_WAVE + lane * 16;
-    const int t_lane = (l32 * L::TSTR + 8 * hf) * 2;
-
-    // dV_j += P^T dO_i and dK_j += dS^T Q_i for the tile in slots (slot2, slot3):
-    // lane = feature column, register = key row
-    auto grad_step = [&](int slot2, int slot3) {
-      const char* fb = smem + slot2 * L::F_BYTES + f_lane;
-      const char* gt = smem + L::GT_OFF + slot3 * L::T_BYTES + t_lane;
-      const char* qt = smem + L::QT_OFF + slot3 * L::T_BYTES + t_lane;
-      bf16x8 pb[2], sbf[2], ga[2][L::NDB], qa[2][L::NDB];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        pb[t] = as_bf16x8(ld16(fb + t * 1024));
-        sbf[t] = as_bf16x8(ld16(fb + (2 + t) * 1024));
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db) {
-          const int toff = (db * 32 * L::TSTR + 16 * t) * 2;
-          ga[t][db] = as_bf16x8(ld16(gt + toff));
-          qa[t][db] = as_bf16x8(ld16(qt + toff));
+          for (int i = 0; i < 4; ++i) stg[i] = bload16(rsrc, ((unsigned)(r0 + 4 * qa + i) * D + fg * 8) * 2u);
         }
-      }
+      };
+      auto lstore = [&](int slot2, int slot3) {     // slots s % 2 and s % 3 of the tile staged
+        if (stager) {
+          char* N = smem + slot2 * L::STAGE + n_off;
+          char* T = smem + slot3 * L::T_BYTES + t_off;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+          for (int i = 0; i < 4; ++i) st16(N + i * L::NB, stg[i]);
 #pragma unroll
-        for (int db = 0; db < L::NDB; ++db) {
-          dv[db] = mfma32(pb[t], ga[t][db], dv[db]);
-          dk[db] = mfma32(sbf[t], qa[t][db], dk[db]);
+          for (int w = 0; w < 4; ++w) {
+            const u32x2 ev = {lo_lo(stg[0][w], stg[1][w]), lo_lo(stg[2][w], stg[3][w])};
+            const u32x2 od = {hi_hi(stg[0][w], stg[1][w]), hi_hi(stg[2][w], stg[3][w])};
+            st8(T + (2 * w) * L::TSTR * 2, ev);
+            st8(T + (2 * w + 1) * L::TSTR * 2, od);
+          }
         }
-      sched_reads_ahead<4 * L::NDB, 4 * L::NDB + 4>();
-    };
+      };
 
-    int tgr = next_tile(it0);                        // the tile of the next gradient step
-    int tg = tgr;                                    // the tile of the next fetch
-    if (n > 0) {
-      gload(tg);
-      lstore(0, 0);
-      tg = next_tile(tg + 1);
-      if (n > 1) {
+      f32x16 dk[L::NDB], dv[L::NDB];
+#pragma unroll
+      for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dk[db][r] = 0.f;
+          dv[db][r] = 0.f;
+        }
+      const int f_lane = L::F_OFF + wq * L::F_WAVE + lane * 16;
+      const int t_lane = (l32 * L::TSTR + 8 * hf) * 2;
+
+      // dV_j += P^T dO_i and dK_j += dS^T Q_i for the tile in slots (slot2, slot3):
+      // lane = feature column, register = key row
+      auto grad_step = [&](int slot2, int slot3) {
+        const char* fb = smem + slot2 * L::F_BYTES + f_lane;
+        const char* gt = smem + L::GT_OFF + slot3 * L::T_BYTES + t_lane;
+        const char* qt = smem + L::QT_OFF + slot3 * L::T_BYTES + t_lane;
+        bf16x8 pb[2], sbf[2], ga[2][L::NDB], qa[2][L::NDB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          pb[t] = as_bf16x8(ld16(fb + t * 1024));
+          sbf[t] = as_bf16x8(ld16(fb + (2 + t) * 1024));
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) {
+            const int toff = (db * 32 * L::TSTR + 16 * t) * 2;
+            ga[t][db] = as_bf16x8(ld16(gt + toff));
+            qa[t][db] = as_bf16x8(ld16(qt + toff));
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) {
+            dv[db] = mfma32(pb[t], ga[t][db], dv[db]);
+            dk[db] = mfma32(sbf[t], qa[t][db], dk[db]);
+          }
+        sched_reads_ahead<4 * L::NDB, 4 * L::NDB + 4>();
+      };
+
+      int tgr = next_tile(it0);                        // the tile of the next gradient step
+      int tg = tgr;                                    // the tile of the next fetch
+      if (n > 0) {
         gload(tg);
+        lstore(0, 0);
         tg = next_tile(tg + 1);
+        if (n > 1) {
+          gload(tg);
+          tg = next_tile(tg + 1);
+        }
       }
-    }
-    wait_lds_all();
-    barrier_keep_vmem();
-    // phase p: gradients of sweep step p-1, stage step p+1, fetch step p+2.
-    // m2 = p % 2 and m3 = p % 3 (wave-uniform counters) pick the slots.
-    int m2 = 0, m3 = 0;
-    for (int p = 0; p < n; ++p) {
-      const int up3 = m3 == 2 ? 0 : m3 + 1;          // (p + 1) % 3
-      const int dn3 = m3 == 0 ? 2 : m3 - 1;          // (p - 1) % 3
-      if (p >= 1) {
-        // causal: a query tile wholly before this wave's keys has all-zero fragments
-        if (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0) grad_step(m2 ^ 1, dn3);
-        tgr = next_tile(tgr + 1);
-      }
-      if (p + 1 < n) lstore(m2 ^ 1, up3);
-      if (p + 2 < n) {
-        gload(tg);
-        tg = next_tile(tg + 1);
-      }
-      // the staged tile is in LDS; the fetch of tile p+2 stays in flight
       wait_lds_all();
       barrier_keep_vmem();
-      m2 ^= 1;
-      m3 = up3;
-    }
-    // the last tile's gradients: its slots are ((n-1) % 2, (n-1) % 3)
-    if (n > 0 && (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0)) grad_step(m2 ^ 1, m3 == 0 ? 2 : m3 - 1);
-
-    // dK_j = scale * dS^T Q and dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
-    const unsigned gsz = grad_f32 ? 4u : 2u;
-    const rsrc_t rdk = make_rsrc(static_cast<char*>(dK) + kbase * gsz, (unsigned)Tk * D * gsz);
-    const rsrc_t rdv = make_rsrc(static_cast<char*>(dV) + kbase * gsz, (unsigned)Tk * D * gsz);
-#pragma unroll
-    for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const unsigned idx = (unsigned)(kw0 + 8 * (r >> 2) + 4 * hf + (r & 3)) * D + db * 32 + l32;
-        const float gk = scale * dk[db][r];
-        const float gv = dv[db][r];   // a scalar copy: bit-casting a vector element in place reads element 0
-        if (grad_f32) {
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gk), rdk, idx * 4u, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gv), rdv, idx * 4u, 0, 0);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(gk, 0.f) & 0xffffu), rdk, idx * 2u, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(gv, 0.f) & 0xffffu), rdv, idx * 2u, 0, 0);
+      // phase p: gradients of sweep step p-1, stage step p+1, fetch step p+2.
+      // m2 = p % 2 and m3 = p % 3 (wave-uniform counters) pick the slots.
+      int m2 = 0, m3 = 0;
+      for (int p = 0; p < n; ++p) {
+        const int up3 = m3 == 2 ? 0 : m3 + 1;          // (p + 1) % 3
+        const int dn3 = m3 == 0 ? 2 : m3 - 1;          // (p - 1) % 3
+        if (p >= 1) {
+          // causal: a query tile wholly before this wave's keys has all-zero fragments
+          if (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0) grad_step(m2 ^ 1, dn3);
+          tgr = next_tile(tgr + 1);
         }
+        if (p + 1 < n) lstore(m2 ^ 1, up3);
+        if (p + 2 < n) {
+          gload(tg);
+          tg = next_tile(tg + 1);
+        }
+        // the staged tile is in LDS; the fetch of tile p+2 stays in flight
+        wait_lds_all();
+        barrier_keep_vmem();
+        m2 ^= 1;
+        m3 = up3;
       }
+      // the last tile's gradients: its slots are ((n-1) % 2, (n-1) % 3)
+      if (n > 0 && (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0)) grad_step(m2 ^ 1, m3 == 0 ? 2 : m3 - 1);
+
+      // dK_j = scale * dS^T Q and dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
+      const unsigned gsz = grad_f32 ? 4u : 2u;
+      const rsrc_t rdk = make_rsrc(static_cast<char*>(dK) + kbase * gsz, (unsigned)Tk * D * gsz);
+      const rsrc_t rdv = make_rsrc(static_cast<char*>(dV) + kbase * gsz, (unsigned)Tk * D * gsz);
+#pragma unroll
+      for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const unsigned idx = (unsigned)(kw0 + 8 * (r >> 2) + 4 * hf + (r & 3)) * D + db * 32 + l32;
+          const float gk = scale * dk[db][r];
+          const float gv = dv[db][r];   // a scalar copy: bit-casting a vector element in place reads element 0
+          if (grad_f32) {
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gk), rdk, idx * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gv), rdv, idx * 4u, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(gk, 0.f) & 0xffffu), rdk, idx * 2u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(gv, 0.f) & 0xffffu), rdv, idx * 2u, 0, 0);
+          }
+        }
+    }
   }
 }
 
@@ -863,268 +880,281 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   __shared__ __attribute__((aligned(1024))) char stage1[L::STAGE];
   auto stage_ptr = [&](int st) -> char* { return st == 0 ? stage0 : stage1; };
 
+  // Plain causal: workgroup p of a head runs query block nqb-1-p, then block
+  // p, so every workgroup sweeps about the same number of key blocks (uneven
+  // workgroups leave CUs waiting on the dispatcher).  Otherwise one block per
+  // workgroup, causal sweeps longest first.
+  constexpr bool PAIRED = CAUSAL && !MASKED && BAND == 0;
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
-  const int bh = lin / nqb;
-  const int qb = CAUSAL ? nqb - 1 - (lin % nqb) : (lin % nqb);    // causal: longest sweeps first
+  const int npb = PAIRED ? (nqb + 1) / 2 : nqb;     // workgroups per head
+  const int bh = lin / npb;
+  const int pidx = lin % npb;
+  const int npass = (PAIRED && 2 * pidx + 1 < nqb) ? 2 : 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
-  const int q0 = qb * L::BR;
-  const int qw = q0 + wave * 32;
-  const int myq = qw + lq;
+  // Every wave runs every block's barriers; the early exit below only skips the
+  // epilogue.  A block's last step ends on a barrier after all its LDS reads, so
+  // the next block's first DMA cannot overwrite a tile still in use.
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qb = !CAUSAL ? pidx : pass == 0 ? nqb - 1 - pidx : pidx;
+    const int q0 = qb * L::BR;
+    const int qw = q0 + wave * 32;
+    const int myq = qw + lq;
 
-  const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
-  const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
-  const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
-  const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
-  const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
-  const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
+    const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+    const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
+    const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
+    const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
+    const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
+    const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
 
-  // Q and dO fragments (B operands): column = query, k = features
-  bf16x8 qf[L::NDS], gf[L::NDS];
+    // Q and dO fragments (B operands): column = query, k = features
+    bf16x8 qf[L::NDS], gf[L::NDS];
 #pragma unroll
-  for (int ds = 0; ds < L::NDS; ++ds) {
-    const unsigned off = ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u;
-    qf[ds] = as_bf16x8(bload16(rq, off));
-    gf[ds] = as_bf16x8(bload16(rg, off));
-  }
-  // -lse log2e and -D of this lane's query; -D seeds every dP^T accumulator
-  const float lnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0));
-  const float dnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
-  f32x16 dseed;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) dseed[r] = dnq;
-
-  int ntile = (Tk + BC - 1) / BC;
-  if (CAUSAL) ntile = min(ntile, (min(q0 + L::BR, Tq) - 1) / BC + 1);
-  int jfirst = 0;                                     // first key block any row of the block can see
-  // BAND: this lane's keys klo .. khi; over the wave's rows, the keys every row
-  // sees (w_lo .. w_hi) and those some row sees (wb_lo .. wb_hi)
-  int klo = 0, khi = 0, w_lo = 0, w_hi = 0, wb_lo = 0, wb_hi = 0;
-  if constexpr (BAND != 0) {
-    const Band<BAND> band{wl, wr, cu, nd, bcausal};
-    band.keys(myq, klo, khi);
-    w_lo = band.lo(qw + 31);
-    w_hi = band.hi(qw);
-    wb_lo = band.lo(qw);
-    wb_hi = band.hi(qw + 31);
-    const int b_hi = band.hi(min(q0 + L::BR, Tq) - 1);
-    ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
-    jfirst = max(0, band.lo(q0)) / BC;
-  }
-
-  // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled
-  const rsrc_t rkv = wave < L::WAVES / 2 ? rk : rv;
-  auto kv_dma = [&](int k0, int st) {
-#pragma unroll
-    for (int i = 0; i < L::KDMA_W; ++i) {
-      const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
-      const int s = (g % L::KDMA) * 64 + lane;
-      const int row = s / L::NC, cp = s % L::NC;
-      const unsigned off = ((unsigned)(k0 + row) * D + (cp ^ dq_swz<L::NC>(row)) * 8) * 2u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rkv, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, off, 0, 0, 0);
+    for (int ds = 0; ds < L::NDS; ++ds) {
+      const unsigned off = ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u;
+      qf[ds] = as_bf16x8(bload16(rq, off));
+      gf[ds] = as_bf16x8(bload16(rg, off));
     }
-  };
-  // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
-  const int swz_l = dq_swz<L::NC>(lq);
-  const int kbase_lane = lq * D * 2 + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
-
-  // ---- K^T operand (A of dQ^T += K^T dS^T): lane l, row feature 32 db + l % 32,
-  // elements = keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3 of key block kb.
-  // Each half comes from one transposing read in which lane 16g + 4e + j
-  // addresses key row 4(g/2) + e (+ 8 for the second half) and features
-  // 16(g%2) + 4j .. +3; tb[sec] is that offset for kb = t = db = 0.
-  const int tg = lane >> 4, ti = lane & 15;
-  int tb[2];
+    // -lse log2e and -D of this lane's query; -D seeds every dP^T accumulator
+    const float lnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0));
+    const float dnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
+    f32x16 dseed;
 #pragma unroll
-  for (int sec = 0; sec < 2; ++sec) {
-    const int row = 8 * sec + 4 * (tg >> 1) + (ti >> 2);
-    const int c = 2 * (tg & 1) + ((ti & 3) >> 1);
-    tb[sec] = row * L::RB + ((c ^ dq_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
-  }
+    for (int r = 0; r < 16; ++r) dseed[r] = dnq;
 
-  f32x16 dq[L::NDB];
-#pragma unroll
-  for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
-
-  // ---- visible key tiles: bit c of word w of mask row a (b) = key block
-  // 64w + c is kept for the first (second) 128 queries.  The words last read
-  // are kept; a cursor moving forward reads again only every 64 key blocks.
-  const int nvw = (nmk + 63) >> 6;
-  const int mr = q0 / kMaskBlock;
-  const bool has_b = L::BR == 2 * kMaskBlock && mr + 1 < (Tq + kMaskBlock - 1) / kMaskBlock;
-  const uint8_t* mrow = MASKED ? bmask + (long long)(bh % H) * mask_hstride + (long long)mr * nmk : nullptr;
-  int cw = -1;
-  unsigned long long ca = 0, cb = 0;
-  auto words = [&](int w) {
-    if (w != cw) {
-      cw = w;
-      ca = mask_word(mrow, 1, nmk, w, lane);
-      cb = has_b ? mask_word(mrow + nmk, 1, nmk, w, lane) : 0ull;
+    int ntile = (Tk + BC - 1) / BC;
+    if (CAUSAL) ntile = min(ntile, (min(q0 + L::BR, Tq) - 1) / BC + 1);
+    int jfirst = 0;                                     // first key block any row of the block can see
+    // BAND: this lane's keys klo .. khi; over the wave's rows, the keys every row
+    // sees (w_lo .. w_hi) and those some row sees (wb_lo .. wb_hi)
+    int klo = 0, khi = 0, w_lo = 0, w_hi = 0, wb_lo = 0, wb_hi = 0;
+    if constexpr (BAND != 0) {
+      const Band<BAND> band{wl, wr, cu, nd, bcausal};
+      band.keys(myq, klo, khi);
+      w_lo = band.lo(qw + 31);
+      w_hi = band.hi(qw);
+      wb_lo = band.lo(qw);
+      wb_hi = band.hi(qw + 31);
+      const int b_hi = band.hi(min(q0 + L::BR, Tq) - 1);
+      ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
+      jfirst = max(0, band.lo(q0)) / BC;
     }
-  };
-  auto next_tile = [&](int j) {                       // first tile >= j either mask row sees, ntile if none
-    if constexpr (MASKED) {
-      if (j >= ntile) return ntile;
-      const int c = j * BC / kMaskBlock;
-      int w = c >> 6;
-      words(w);
-      unsigned long long bits = (ca | cb) & (~0ull << (c & 63));
-      while (bits == 0) {
-        if (++w >= nvw) return ntile;
+
+    // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled
+    const rsrc_t rkv = wave < L::WAVES / 2 ? rk : rv;
+    auto kv_dma = [&](int k0, int st) {
+#pragma unroll
+      for (int i = 0; i < L::KDMA_W; ++i) {
+        const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
+        const int s = (g % L::KDMA) * 64 + lane;
+        const int row = s / L::NC, cp = s % L::NC;
+        const unsigned off = ((unsigned)(k0 + row) * D + (cp ^ dq_swz<L::NC>(row)) * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rkv, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, off, 0, 0, 0);
+      }
+    };
+    // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
+    const int swz_l = dq_swz<L::NC>(lq);
+    const int kbase_lane = lq * D * 2 + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
+
+    // ---- K^T operand (A of dQ^T += K^T dS^T): lane l, row feature 32 db + l % 32,
+    // elements = keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3 of key block kb.
+    // Each half comes from one transposing read in which lane 16g + 4e + j
+    // addresses key row 4(g/2) + e (+ 8 for the second half) and features
+    // 16(g%2) + 4j .. +3; tb[sec] is that offset for kb = t = db = 0.
+    const int tg = lane >> 4, ti = lane & 15;
+    int tb[2];
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int row = 8 * sec + 4 * (tg >> 1) + (ti >> 2);
+      const int c = 2 * (tg & 1) + ((ti & 3) >> 1);
+      tb[sec] = row * L::RB + ((c ^ dq_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
+    }
+
+    f32x16 dq[L::NDB];
+#pragma unroll
+    for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+
+    // ---- visible key tiles: bit c of word w of mask row a (b) = key block
+    // 64w + c is kept for the first (second) 128 queries.  The words last read
+    // are kept; a cursor moving forward reads again only every 64 key blocks.
+    const int nvw = (nmk + 63) >> 6;
+    const int mr = q0 / kMaskBlock;
+    const bool has_b = L::BR == 2 * kMaskBlock && mr + 1 < (Tq + kMaskBlock - 1) / kMaskBlock;
+    const uint8_t* mrow = MASKED ? bmask + (long long)(bh % H) * mask_hstride + (long long)mr * nmk : nullptr;
+    int cw = -1;
+    unsigned long long ca = 0, cb = 0;
+    auto words = [&](int w) {
+      if (w != cw) {
+        cw = w;
+        ca = mask_word(mrow, 1, nmk, w, lane);
+        cb = has_b ? mask_word(mrow + nmk, 1, nmk, w, lane) : 0ull;
+      }
+    };
+    auto next_tile = [&](int j) {                       // first tile >= j either mask row sees, ntile if none
+      if constexpr (MASKED) {
+        if (j >= ntile) return ntile;
+        const int c = j * BC / kMaskBlock;
+        int w = c >> 6;
         words(w);
-        bits = ca | cb;
+        unsigned long long bits = (ca | cb) & (~0ull << (c & 63));
+        while (bits == 0) {
+          if (++w >= nvw) return ntile;
+          words(w);
+          bits = ca | cb;
+        }
+        const int c2 = w * 64 + (int)__builtin_ctzll(bits);
+        return c2 == c ? j : min(ntile, c2 * (kMaskBlock / BC));
+      } else {
+        return j;
       }
-      const int c2 = w * 64 + (int)__builtin_ctzll(bits);
-      return c2 == c ? j : min(ntile, c2 * (kMaskBlock / BC));
-    } else {
-      return j;
-    }
-  };
-  auto wave_sees = [&](int j) {                       // this wave's mask row sees tile j
-    if constexpr (MASKED) {
-      const int c = j * BC / kMaskBlock;
-      words(c >> 6);
-      return ((((wave >> 2) ? cb : ca) >> (c & 63)) & 1ull) != 0;
-    } else {
-      return true;
-    }
-  };
-
-  auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
-  const int j0 = next_tile(jfirst);
-  kv_dma(first_row(j0), 0);
-  wait_vmem_all();
-  __syncthreads();
-
-  // tile j in stage ST (the step's parity in the sweep); jn is the tile after it
-  auto step = [&](int j, int jn, int ST) {
-    // the mask test comes before the loads of block jn: a branch between those
-    // loads and the reads of stage ST would make the compiler wait for the loads
-    const bool sees = wave_sees(j);
-    kv_dma(first_row(jn), ST ^ 1);
-    const int kt0 = j * BC;
-    const bool in_band = BAND == 0 || (kt0 <= wb_hi && kt0 + BC - 1 >= wb_lo);
-    if ((!CAUSAL || kt0 <= qw + 31) && sees && in_band) {   // some key of the block is visible to this wave
-      const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk) ||
-                        (BAND != 0 && !(kt0 >= w_lo && kt0 + BC - 1 <= w_hi));
-#pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb) {
-        // S^T and dP^T - D for 32 keys: register r = key kt0 + 32 kb + 8(r/4)+4hf+r%4, lane = query
-        f32x16 s, dp = dseed;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-        bf16x8 ka[L::NDS], va[L::NDS];
-#pragma unroll
-        for (int ds = 0; ds < L::NDS; ++ds) {
-          const int off = kb * 32 * D * 2 + (kbase_lane ^ (ds << 5));
-          ka[ds] = as_bf16x8(ld16(stage_ptr(ST) + L::K_OFF + off));
-          va[ds] = as_bf16x8(ld16(stage_ptr(ST) + L::V_OFF + off));
-        }
-#pragma unroll
-        for (int ds = 0; ds < L::NDS; ++ds) {
-          s = mfma32(ka[ds], qf[ds], s);
-          dp = mfma32(va[ds], gf[ds], dp);
-        }
-        sched_reads_ahead<2 * L::NDS>();
-        // K^T operands of the dQ product for k-step t = 0, read now so that their
-        // latency hides behind the softmax (all of them at once would spill)
-        const char* ks = stage_ptr(ST) + L::K_OFF + kb * 32 * L::RB;
-        bf16x8 ta[2][L::NDB];
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db) {
-          const u32x2 lo = ld8_tr(ks + (tb[0] ^ (db << 6)));
-          const u32x2 hi = ld8_tr(ks + (tb[1] ^ (db << 6)));
-          ta[0][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        }
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, lnq));
-        if (edge) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= Tk || (CAUSAL && key > myq) || (BAND != 0 && (key < klo || key > khi))) p[r] = 0.f;
-          }
-        }
-        bf16x8 sf[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * t + 2 * e;
-            w[e] = pack_bf16(p[r] * dp[r], p[r + 1] * dp[r + 1]);
-          }
-          sf[t] = as_bf16x8(w);
-        }
-        // dQ^T += K_j^T dS^T: lane = query column, register = feature row (the
-        // operands of k-step t = 1 are read here)
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db) {
-          const u32x2 lo = ld8_tr(ks + 16 * L::RB + (tb[0] ^ (db << 6)));
-          const u32x2 hi = ld8_tr(ks + 16 * L::RB + (tb[1] ^ (db << 6)));
-          ta[1][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int db = 0; db < L::NDB; ++db) dq[db] = mfma32(ta[t][db], sf[t], dq[db]);
+    };
+    auto wave_sees = [&](int j) {                       // this wave's mask row sees tile j
+      if constexpr (MASKED) {
+        const int c = j * BC / kMaskBlock;
+        words(c >> 6);
+        return ((((wave >> 2) ? cb : ca) >> (c & 63)) & 1ull) != 0;
+      } else {
+        return true;
       }
-    }
+    };
+
+    auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
+    const int j0 = next_tile(jfirst);
+    kv_dma(first_row(j0), 0);
     wait_vmem_all();
     __syncthreads();
-  };
 
-  // The three loop forms compile differently; each is used where it needs no
-  // spills.  d <= 128 unrolls two steps so that every stage offset is a
-  // constant; d = 256 runs one step per iteration with the stage offset
-  // computed at run time.
-  if constexpr (D == 256) {
-    for (int j = j0, st = 0; j < ntile; st ^= 1) {
-      const int jn = next_tile(j + 1);
-      step(j, jn, st);
-      j = jn;
-    }
-  } else if constexpr (MASKED) {
-    for (int j = j0; j < ntile;) {
-      int jn = next_tile(j + 1);
-      step(j, jn, 0);
-      j = jn;
-      if (j >= ntile) break;
-      jn = next_tile(j + 1);
-      step(j, jn, 1);
-      j = jn;
-    }
-  } else {
-    for (int j = j0; j < ntile; j += 2) {
-      step(j, j + 1, 0);
-      if (j + 1 < ntile) step(j + 1, j + 2, 1);
-    }
-  }
+    // tile j in stage ST (the step's parity in the sweep); jn is the tile after it
+    auto step = [&](int j, int jn, int ST) {
+      // the mask test comes before the loads of block jn: a branch between those
+      // loads and the reads of stage ST would make the compiler wait for the loads
+      const bool sees = wave_sees(j);
+      kv_dma(first_row(jn), ST ^ 1);
+      const int kt0 = j * BC;
+      const bool in_band = BAND == 0 || (kt0 <= wb_hi && kt0 + BC - 1 >= wb_lo);
+      if ((!CAUSAL || kt0 <= qw + 31) && sees && in_band) {   // some key of the block is visible to this wave
+        const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk) ||
+                          (BAND != 0 && !(kt0 >= w_lo && kt0 + BC - 1 <= w_hi));
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb) {
+          // S^T and dP^T - D for 32 keys: register r = key kt0 + 32 kb + 8(r/4)+4hf+r%4, lane = query
+          f32x16 s, dp = dseed;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = 0.f;
+          bf16x8 ka[L::NDS], va[L::NDS];
+#pragma unroll
+          for (int ds = 0; ds < L::NDS; ++ds) {
+            const int off = kb * 32 * D * 2 + (kbase_lane ^ (ds << 5));
+            ka[ds] = as_bf16x8(ld16(stage_ptr(ST) + L::K_OFF + off));
+            va[ds] = as_bf16x8(ld16(stage_ptr(ST) + L::V_OFF + off));
+          }
+#pragma unroll
+          for (int ds = 0; ds < L::NDS; ++ds) {
+            s = mfma32(ka[ds], qf[ds], s);
+            dp = mfma32(va[ds], gf[ds], dp);
+          }
+          sched_reads_ahead<2 * L::NDS>();
+          // K^T operands of the dQ product for k-step t = 0, read now so that their
+          // latency hides behind the softmax (all of them at once would spill)
+          const char* ks = stage_ptr(ST) + L::K_OFF + kb * 32 * L::RB;
+          bf16x8 ta[2][L::NDB];
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) {
+            const u32x2 lo = ld8_tr(ks + (tb[0] ^ (db << 6)));
+            const u32x2 hi = ld8_tr(ks + (tb[1] ^ (db << 6)));
+            ta[0][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          }
+          float p[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, lnq));
+          if (edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (key >= Tk || (CAUSAL && key > myq) || (BAND != 0 && (key < klo || key > khi))) p[r] = 0.f;
+            }
+          }
+          bf16x8 sf[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * t + 2 * e;
+              w[e] = pack_bf16(p[r] * dp[r], p[r + 1] * dp[r + 1]);
+            }
+            sf[t] = as_bf16x8(w);
+          }
+          // dQ^T += K_j^T dS^T: lane = query column, register = feature row (the
+          // operands of k-step t = 1 are read here)
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) {
+            const u32x2 lo = ld8_tr(ks + 16 * L::RB + (tb[0] ^ (db << 6)));
+            const u32x2 hi = ld8_tr(ks + 16 * L::RB + (tb[1] ^ (db << 6)));
+            ta[1][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int db = 0; db < L::NDB; ++db) dq[db] = mfma32(ta[t][db], sf[t], dq[db]);
+        }
+      }
+      wait_vmem_all();
+      __syncthreads();
+    };
 
-  if (myq >= Tq) return;
-  // dQ: lane = query, register 4g+e of block db = feature db*32 + 8g + 4hf + e
-#pragma unroll
-  for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = db * 32 + 8 * g + 4 * hf;
-      const size_t off = qbase + (size_t)myq * D + d0;
-      const float v0 = scale * dq[db][4 * g], v1 = scale * dq[db][4 * g + 1];
-      const float v2 = scale * dq[db][4 * g + 2], v3 = scale * dq[db][4 * g + 3];
-      if (grad_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(dQ) + off) = (f32x4){v0, v1, v2, v3};
-      } else {
-        const u32x2 w = {pack_bf16(v0, v1), pack_bf16(v2, v3)};
-        st8(static_cast<uint16_t*>(dQ) + off, w);
+    // The three loop forms compile differently; each is used where it needs no
+    // spills.  d <= 128 unrolls two steps so that every stage offset is a
+    // constant; d = 256 runs one step per iteration with the stage offset
+    // computed at run time.
+    if constexpr (D == 256) {
+      for (int j = j0, st = 0; j < ntile; st ^= 1) {
+        const int jn = next_tile(j + 1);
+        step(j, jn, st);
+        j = jn;
+      }
+    } else if constexpr (MASKED) {
+      for (int j = j0; j < ntile;) {
+        int jn = next_tile(j + 1);
+        step(j, jn, 0);
+        j = jn;
+        if (j >= ntile) break;
+        jn = next_tile(j + 1);
+        step(j, jn, 1);
+        j = jn;
+      }
+    } else {
+      for (int j = j0; j < ntile; j += 2) {
+        step(j, j + 1, 0);
+        if (j + 1 < ntile) step(j + 1, j + 2, 1);
       }
     }
+
+    if (myq >= Tq) continue;
+    // dQ: lane = query, register 4g+e of block db = feature db*32 + 8g + 4hf + e
+#pragma unroll
+    for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hf;
+        const size_t off = qbase + (size_t)myq * D + d0;
+        const float v0 = scale * dq[db][4 * g], v1 = scale * dq[db][4 * g + 1];
+        const float v2 = scale * dq[db][4 * g + 2], v3 = scale * dq[db][4 * g + 3];
+        if (grad_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(dQ) + off) = (f32x4){v0, v1, v2, v3};
+        } else {
+          const u32x2 w = {pack_bf16(v0, v1), pack_bf16(v2, v3)};
+          st8(static_cast<uint16_t*>(dQ) + off, w);
+        }
+      }
+  }
 }
 
 template <int D>
@@ -1163,8 +1193,11 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
   if (phases & FA_BWD_MAIN) {
     // key-block sweep: 8 waves in two roles for d <= 128, 4 waves for d = 256
     constexpr int KV_THREADS = D == 256 ? 256 : 512;
+    // plain causal, d = 128: key blocks p and nkb-1-p share a workgroup
+    const bool paired = D == 128 && causal && !bmask && band == 0;
+    const long long nkv = paired ? (long long)((nkb + 1) / 2) * B * H : nblk;
     auto kv = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, dim3((unsigned)nblk), dim3(KV_THREADS), 0, stream, q, k, v, g, Ln, Dn, dK, dV, Tq,
+      hipLaunchKernelGGL(kernel, dim3((unsigned)nkv), dim3(KV_THREADS), 0, stream, q, k, v, g, Ln, Dn, dK, dV, Tq,
                          Tk, scale, cl2e, nkb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
     };
     if constexpr (D == 256) {
@@ -1190,8 +1223,11 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
     }
   }
   if (phases & FA_BWD_POST) {
+    // plain causal: query blocks nqb-1-p and p share a workgroup
+    const bool paired = causal && !bmask && band == 0;
+    const long long ndq = paired ? (long long)((nqb + 1) / 2) * B * H : nqblk;
     auto dqk = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, dim3((unsigned)nqblk), dim3(LQ::THREADS), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq,
+      hipLaunchKernelGGL(kernel, dim3((unsigned)ndq), dim3(LQ::THREADS), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq,
                          Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
     };
     if (band == 1) dqk(bwd_dq_kernel<D, false, false, 1>);

@@ -106,323 +106,337 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     else return stage1;
   };
 
-  // Workgroup -> (head, query block).  Consecutive workgroup ids go to
+  // Workgroup -> (head, query blocks).  Consecutive workgroup ids go to
   // different XCDs round-robin; remapping gives each XCD a contiguous range of
   // logical blocks, so one head's query blocks (which share K and V) run on
-  // the same L2.  Within a head the longest causal blocks start first.
+  // the same L2.
+  // Plain causal: workgroup p of a head runs query block nqb-1-p, then block p,
+  // so every workgroup sweeps about the same number of key tiles.  With one
+  // block each, lengths range from 1 to nqb blocks' worth, and the dispatcher
+  // leaves CUs with a free slot idle for tens of microseconds at a time.
+  // Otherwise one block per workgroup, the longest causal blocks first.
+  constexpr bool PAIRED = CAUSAL && !MASKED && BAND == 0;
   const int nblk = gridDim.x;
   const int wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
-  const int bh = lin / nqb;
-  const int qb = nqb - 1 - (lin % nqb);
+  const int npb = PAIRED ? (nqb + 1) / 2 : nqb;     // workgroups per head
+  const int bh = lin / npb;
+  const int pidx = lin % npb;
+  const int npass = (PAIRED && 2 * pidx + 1 < nqb) ? 2 : 1;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hf = lane >> 5;
   const size_t qbase = (size_t)bh * Tq * D;
   const size_t kbase = (size_t)bh * Tk * D;
-  const int q0 = qb * kBR;
-  const int qw = q0 + wave * 32;
-  const int myq = qw + lq;
+  // Every wave runs every block's barriers; the early exits below only skip the
+  // epilogue.  A block's last step ends on a barrier after all its LDS reads, so
+  // the next block's first DMA cannot overwrite a tile still in use.
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qb = pass == 0 ? nqb - 1 - pidx : pidx;
+    const int q0 = qb * kBR;
+    const int qw = q0 + wave * 32;
+    const int myq = qw + lq;
 
-  // Per-head buffer resources: rows past Tq / Tk read as zeros.
-  const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
-  const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
-  const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
+    // Per-head buffer resources: rows past Tq / Tk read as zeros.
+    const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+    const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
+    const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
 
-  // Q fragments (B operand of S^T = K Q^T): column = query, k = features.
-  bf16x8 qf[L::NDS];
-#pragma unroll
-  for (int ds = 0; ds < L::NDS; ++ds)
-    qf[ds] = as_bf16x8(bload16(rq, ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u));
-
-  int ntile = (Tk + BC - 1) / BC;
-  if (CAUSAL) ntile = min(ntile, (min(q0 + kBR, Tq) - 1) / BC + 1);
-  int jfirst = 0;                     // first key block any row of the block can see
-  // BAND: this lane's keys klo .. khi; over the wave's rows the largest lo and
-  // the smallest hi (a tile between them needs no element mask)
-  int klo = 0, khi = 0, w_lo = 0, w_hi = 0;
-  if constexpr (BAND != 0) {
-    const Band<BAND> band{wl, wr, cu, nd, bcausal};
-    band.keys(myq, klo, khi);
-    w_lo = band.lo(qw + 31);
-    w_hi = band.hi(qw);
-    const int b_hi = band.hi(min(q0 + kBR, Tq) - 1);
-    ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
-    jfirst = max(0, band.lo(q0)) / BC;
-  }
-
-  // ---- K and V: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
-  auto k_dma = [&](int k0, char* kst) {
-#pragma unroll
-    for (int i = 0; i < L::KDMA_W; ++i) {
-      const int g = wave * L::KDMA_W + i;
-      const int s = g * 64 + lane;
-      const int row = s / L::NC, cp = s % L::NC;
-      const int src = cp ^ kswz<L::NC>(row);
-      const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(kst + g * 1024), 16, off, 0, 0, 0);
-    }
-  };
-  auto v_dma = [&](int k0, char* vst) {
-#pragma unroll
-    for (int i = 0; i < L::KDMA_W; ++i) {
-      const int g = wave * L::KDMA_W + i;
-      const int s = g * 64 + lane;
-      const int row = s / L::NC, cp = s % L::NC;
-      const int src = cp ^ vswz<L::NC>(row);
-      const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)(vst + g * 1024), 16, off, 0, 0, 0);
-    }
-  };
-  // Per-lane K read offset (bytes, relative to a stage and a 32-key block) for
-  // k-step ds: chunk (2 ds + hf) ^ swz of row lq.  The XOR only touches bits 5..7
-  // of kbase_lane (rows are >= 128 bytes), so each k-step is kbase_lane ^ (ds << 5).
-  const int kswz_l = kswz<L::NC>(lq);
-  const int kbase_lane = lq * D * 2 + (((kswz_l >> 1) << 5) | ((hf ^ (kswz_l & 1)) << 4));
-
-  // ---- V^T operand (A of O^T += V^T P^T): lane l, row feature 32 db + l % 32,
-  // elements = keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3 of key block kb,
-  // the order of the P fragment's k-slots.  Each comes from one transposing read
-  // in which lane 16g + 4e + j addresses key row 4(g/2) + e and features
-  // 16(g%2) + 4j .. +3 (plus 32kb + 16t, and 8 for the second read).
-  const int vg = lane >> 4, vi = lane & 15;
-  const int vrow = 4 * (vg >> 1) + (vi >> 2);
-  const int vc0 = 2 * (vg & 1) + ((vi & 3) >> 1);
-  const int vlane = vrow * L::RB + ((vc0 ^ vswz<L::NC>(vrow)) << 4) + 8 * (vi & 1);
-
-  f32x16 o[L::NDB];
-#pragma unroll
-  for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_ref = -INFINITY;   // reference maximum, scale*log2(e) units
-  float l_part = 0.f;        // this lane's share of the sum of the weights
-  float lr_part = 0.f;       // ... and of the bf16-rounded weights
-
-  auto s_product = [&](f32x16 (&s)[L::NKB], const char* kst) {
-#pragma unroll
-    for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    bf16x8 ka[L::NDS][L::NKB];
+    // Q fragments (B operand of S^T = K Q^T): column = query, k = features.
+    bf16x8 qf[L::NDS];
 #pragma unroll
     for (int ds = 0; ds < L::NDS; ++ds)
-#pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb)
-        ka[ds][kb] = as_bf16x8(ld16(kst + kb * 32 * D * 2 + (kbase_lane ^ (ds << 5))));
-#pragma unroll
-    for (int ds = 0; ds < L::NDS; ++ds)
-#pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb) s[kb] = mfma32(ka[ds][kb], qf[ds], s[kb]);
-    sched_reads_ahead<L::NDS * L::NKB>();
-  };
-  auto mask_tile = [&](f32x16 (&s)[L::NKB], int j) {
-    const int k0 = j * BC;
+      qf[ds] = as_bf16x8(bload16(rq, ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u));
+
+    int ntile = (Tk + BC - 1) / BC;
+    if (CAUSAL) ntile = min(ntile, (min(q0 + kBR, Tq) - 1) / BC + 1);
+    int jfirst = 0;                     // first key block any row of the block can see
+    // BAND: this lane's keys klo .. khi; over the wave's rows the largest lo and
+    // the smallest hi (a tile between them needs no element mask)
+    int klo = 0, khi = 0, w_lo = 0, w_hi = 0;
     if constexpr (BAND != 0) {
-      // inside the band of every row of the wave: no element mask needed
-      if (k0 >= w_lo && k0 + BC - 1 <= w_hi && k0 + BC <= Tk) return;
-#pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= Tk || key < klo || key > khi) s[kb][r] = -INFINITY;
-        }
-      return;
+      const Band<BAND> band{wl, wr, cu, nd, bcausal};
+      band.keys(myq, klo, khi);
+      w_lo = band.lo(qw + 31);
+      w_hi = band.hi(qw);
+      const int b_hi = band.hi(min(q0 + kBR, Tq) - 1);
+      ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
+      jfirst = max(0, band.lo(q0)) / BC;
     }
-    if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk)) {
-#pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= Tk || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
-        }
-    }
-  };
 
-  // Key blocks the sweep visits: all of them, or (block mask, [ZtF] "Dropout,
-  // block-sparsity, and other real-kernel details") only those whose 128-key
-  // mask block is kept for this 128-row block; next_tile(j) is the first
-  // visited block at or after j (ntile when none is left).  The mask row is
-  // read 64 blocks at a time as a bit word held in scalar registers.
-  static_assert(kBR == 128 && 128 % BC == 0, "one mask row per query block, whole key blocks per mask block");
-  const uint8_t* mrow = MASKED ? bmask + (bh % H) * mask_hstride + (long long)qb * nmk : nullptr;
-  const int nvw = (nmk + 63) >> 6;
-  int cw = -1;
-  unsigned long long cbits = 0;
-  auto word = [&](int w) {
-    if (w != cw) {
-      cw = w;
-      cbits = mask_word(mrow, 1, nmk, w, lane);
-    }
-    return cbits;
-  };
-  auto next_tile = [&](int j) {
-    if constexpr (MASKED) {
-      if (j >= ntile) return ntile;
-      const int c = (j * BC) >> 7;
-      int w = c >> 6;
-      unsigned long long bits = word(w) & (~0ull << (c & 63));
-      while (bits == 0) {
-        if (++w >= nvw) return ntile;
-        bits = word(w);
+    // ---- K and V: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
+    auto k_dma = [&](int k0, char* kst) {
+#pragma unroll
+      for (int i = 0; i < L::KDMA_W; ++i) {
+        const int g = wave * L::KDMA_W + i;
+        const int s = g * 64 + lane;
+        const int row = s / L::NC, cp = s % L::NC;
+        const int src = cp ^ kswz<L::NC>(row);
+        const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(kst + g * 1024), 16, off, 0, 0, 0);
       }
-      const int c2 = w * 64 + (int)__builtin_ctzll(bits);
-      return c2 == c ? j : min(ntile, (c2 << 7) / BC);
-    } else {
-      return j;
-    }
-  };
+    };
+    auto v_dma = [&](int k0, char* vst) {
+#pragma unroll
+      for (int i = 0; i < L::KDMA_W; ++i) {
+        const int g = wave * L::KDMA_W + i;
+        const int s = g * 64 + lane;
+        const int row = s / L::NC, cp = s % L::NC;
+        const int src = cp ^ vswz<L::NC>(row);
+        const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(vst + g * 1024), 16, off, 0, 0, 0);
+      }
+    };
+    // Per-lane K read offset (bytes, relative to a stage and a 32-key block) for
+    // k-step ds: chunk (2 ds + hf) ^ swz of row lq.  The XOR only touches bits 5..7
+    // of kbase_lane (rows are >= 128 bytes), so each k-step is kbase_lane ^ (ds << 5).
+    const int kswz_l = kswz<L::NC>(lq);
+    const int kbase_lane = lq * D * 2 + (((kswz_l >> 1) << 5) | ((hf ^ (kswz_l & 1)) << 4));
 
-  // ---- prologue: the first visited K and V block into LDS stage 0
-  // A block index past the sweep maps to row Tk: its loads return zeros and
-  // move no data, so the steps below need no branches around their loads.
-  auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
-  const int j0 = next_tile(jfirst);
-  k_dma(first_row(j0), stage_ptr(std::integral_constant<int, 0>{}) + L::K_OFF);
-  v_dma(first_row(j0), stage_ptr(std::integral_constant<int, 0>{}) + L::V_OFF);
-  wait_vmem_all();
-  __syncthreads();
+    // ---- V^T operand (A of O^T += V^T P^T): lane l, row feature 32 db + l % 32,
+    // elements = keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3 of key block kb,
+    // the order of the P fragment's k-slots.  Each comes from one transposing read
+    // in which lane 16g + 4e + j addresses key row 4(g/2) + e and features
+    // 16(g%2) + 4j .. +3 (plus 32kb + 16t, and 8 for the second read).
+    const int vg = lane >> 4, vi = lane & 15;
+    const int vrow = 4 * (vg >> 1) + (vi >> 2);
+    const int vc0 = 2 * (vg & 1) + ((vi & 3) >> 1);
+    const int vlane = vrow * L::RB + ((vc0 ^ vswz<L::NC>(vrow)) << 4) + 8 * (vi & 1);
 
-  auto step = [&](int j, int jn, auto stage) {
-    constexpr int ST = decltype(stage)::value;        // position of block j in the sweep, mod 2
-    // the next visited block jn in flight, straight into the other LDS stage
-    char* const cur = stage_ptr(std::integral_constant<int, ST>{});
-    char* const nxt = stage_ptr(std::integral_constant<int, ST ^ 1>{});
-    k_dma(first_row(jn), nxt + L::K_OFF);
-    v_dma(first_row(jn), nxt + L::V_OFF);
-    f32x16 s[L::NKB];
-    s_product(s, cur + L::K_OFF);
-    // V^T operands of the PV product.  For d <= 128 they are read here, so that
-    // their latency hides behind the softmax; at d = 256 (one wave per SIMD, all
-    // registers in use) holding them that long costs more than it hides.
-    const char* vs = cur + L::V_OFF;
-    bf16x8 va[L::NKB][2][L::NDB];
-    auto read_va = [&]() {
+    f32x16 o[L::NDB];
+#pragma unroll
+    for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_ref = -INFINITY;   // reference maximum, scale*log2(e) units
+    float l_part = 0.f;        // this lane's share of the sum of the weights
+    float lr_part = 0.f;       // ... and of the bf16-rounded weights
+
+    auto s_product = [&](f32x16 (&s)[L::NKB], const char* kst) {
+#pragma unroll
+      for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      bf16x8 ka[L::NDS][L::NKB];
+#pragma unroll
+      for (int ds = 0; ds < L::NDS; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb)
+          ka[ds][kb] = as_bf16x8(ld16(kst + kb * 32 * D * 2 + (kbase_lane ^ (ds << 5))));
+#pragma unroll
+      for (int ds = 0; ds < L::NDS; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb) s[kb] = mfma32(ka[ds][kb], qf[ds], s[kb]);
+      sched_reads_ahead<L::NDS * L::NKB>();
+    };
+    auto mask_tile = [&](f32x16 (&s)[L::NKB], int j) {
+      const int k0 = j * BC;
+      if constexpr (BAND != 0) {
+        // inside the band of every row of the wave: no element mask needed
+        if (k0 >= w_lo && k0 + BC - 1 <= w_hi && k0 + BC <= Tk) return;
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= Tk || key < klo || key > khi) s[kb][r] = -INFINITY;
+          }
+        return;
+      }
+      if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk)) {
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= Tk || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
+          }
+      }
+    };
+
+    // Key blocks the sweep visits: all of them, or (block mask, [ZtF] "Dropout,
+    // block-sparsity, and other real-kernel details") only those whose 128-key
+    // mask block is kept for this 128-row block; next_tile(j) is the first
+    // visited block at or after j (ntile when none is left).  The mask row is
+    // read 64 blocks at a time as a bit word held in scalar registers.
+    static_assert(kBR == 128 && 128 % BC == 0, "one mask row per query block, whole key blocks per mask block");
+    const uint8_t* mrow = MASKED ? bmask + (bh % H) * mask_hstride + (long long)qb * nmk : nullptr;
+    const int nvw = (nmk + 63) >> 6;
+    int cw = -1;
+    unsigned long long cbits = 0;
+    auto word = [&](int w) {
+      if (w != cw) {
+        cw = w;
+        cbits = mask_word(mrow, 1, nmk, w, lane);
+      }
+      return cbits;
+    };
+    auto next_tile = [&](int j) {
+      if constexpr (MASKED) {
+        if (j >= ntile) return ntile;
+        const int c = (j * BC) >> 7;
+        int w = c >> 6;
+        unsigned long long bits = word(w) & (~0ull << (c & 63));
+        while (bits == 0) {
+          if (++w >= nvw) return ntile;
+          bits = word(w);
+        }
+        const int c2 = w * 64 + (int)__builtin_ctzll(bits);
+        return c2 == c ? j : min(ntile, (c2 << 7) / BC);
+      } else {
+        return j;
+      }
+    };
+
+    // ---- prologue: the first visited K and V block into LDS stage 0
+    // A block index past the sweep maps to row Tk: its loads return zeros and
+    // move no data, so the steps below need no branches around their loads.
+    auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
+    const int j0 = next_tile(jfirst);
+    k_dma(first_row(j0), stage_ptr(std::integral_constant<int, 0>{}) + L::K_OFF);
+    v_dma(first_row(j0), stage_ptr(std::integral_constant<int, 0>{}) + L::V_OFF);
+    wait_vmem_all();
+    __syncthreads();
+
+    auto step = [&](int j, int jn, auto stage) {
+      constexpr int ST = decltype(stage)::value;        // position of block j in the sweep, mod 2
+      // the next visited block jn in flight, straight into the other LDS stage
+      char* const cur = stage_ptr(std::integral_constant<int, ST>{});
+      char* const nxt = stage_ptr(std::integral_constant<int, ST ^ 1>{});
+      k_dma(first_row(jn), nxt + L::K_OFF);
+      v_dma(first_row(jn), nxt + L::V_OFF);
+      f32x16 s[L::NKB];
+      s_product(s, cur + L::K_OFF);
+      // V^T operands of the PV product.  For d <= 128 they are read here, so that
+      // their latency hides behind the softmax; at d = 256 (one wave per SIMD, all
+      // registers in use) holding them that long costs more than it hides.
+      const char* vs = cur + L::V_OFF;
+      bf16x8 va[L::NKB][2][L::NDB];
+      auto read_va = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int db = 0; db < L::NDB; ++db) {
+              const char* p = vs + (32 * kb + 16 * t) * L::RB + (vlane ^ (db << 6));
+              const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
+              va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+      };
+      if constexpr (D <= 128) read_va();
+      mask_tile(s, j);
+      // row maximum and (below) row sums as shallow trees of independent partial
+      // results: long chains of dependent vector ops leave the wave stalled
+      float mq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // chain q folds s[kb][4q .. 4q+3] for every kb, two new values per max3
+        float m = max3f(s[0][4 * q], s[0][4 * q + 1], s[0][4 * q + 2]);
+        float pend = s[0][4 * q + 3];
+        bool has = true;
+#pragma unroll
+        for (int kb = 1; kb < L::NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (has) m = max3f(m, pend, s[kb][4 * q + e]);
+            else pend = s[kb][4 * q + e];
+            has = !has;
+          }
+        mq[q] = has ? max2f(m, pend) : m;
+      }
+      float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
+      mx = half_swap_max(mx) * cl2e;
+      const bool grow = mx > m_ref + kRescaleSlack;     // never true for a row with no visible key yet
+      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+        const float alpha = grow ? fast_exp2(m_ref - mx) : 1.f;   // 0 on a row's first block
+        if (grow) m_ref = mx;
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        l_part *= alpha;
+        lr_part *= alpha;
+      }
+      const float mneg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+      // P~ rounded to bf16 for the PV product; both sums updated
+      bf16x8 pf[L::NKB][2];
+      float ps[4] = {0.f, 0.f, 0.f, 0.f}, prs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < L::NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * t + 2 * e;
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], cl2e, mneg));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cl2e, mneg));
+            ps[e] += p0 + p1;
+            w[e] = pack_bf16(p0, p1);
+            prs[e] = add_bf16_pair(w[e], prs[e]);
+          }
+          pf[kb][t] = as_bf16x8(w);
+        }
+      l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
+      // O~^T += V_j^T P~_j^T (independent accumulators back to back)
+      if constexpr (D > 128) read_va();
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int db = 0; db < L::NDB; ++db) {
-            const char* p = vs + (32 * kb + 16 * t) * L::RB + (vlane ^ (db << 6));
-            const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
-            va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          }
+          for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
+      if constexpr (D > 128) sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
+      wait_vmem_all();
+      __syncthreads();
     };
-    if constexpr (D <= 128) read_va();
-    mask_tile(s, j);
-    // row maximum and (below) row sums as shallow trees of independent partial
-    // results: long chains of dependent vector ops leave the wave stalled
-    float mq[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // chain q folds s[kb][4q .. 4q+3] for every kb, two new values per max3
-      float m = max3f(s[0][4 * q], s[0][4 * q + 1], s[0][4 * q + 2]);
-      float pend = s[0][4 * q + 3];
-      bool has = true;
-#pragma unroll
-      for (int kb = 1; kb < L::NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (has) m = max3f(m, pend, s[kb][4 * q + e]);
-          else pend = s[kb][4 * q + e];
-          has = !has;
-        }
-      mq[q] = has ? max2f(m, pend) : m;
-    }
-    float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
-    mx = half_swap_max(mx) * cl2e;
-    const bool grow = mx > m_ref + kRescaleSlack;     // never true for a row with no visible key yet
-    if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
-      const float alpha = grow ? fast_exp2(m_ref - mx) : 1.f;   // 0 on a row's first block
-      if (grow) m_ref = mx;
-#pragma unroll
-      for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      l_part *= alpha;
-      lr_part *= alpha;
-    }
-    const float mneg = (m_ref == -INFINITY) ? 0.f : -m_ref;
-    // P~ rounded to bf16 for the PV product; both sums updated
-    bf16x8 pf[L::NKB][2];
-    float ps[4] = {0.f, 0.f, 0.f, 0.f}, prs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 8 * t + 2 * e;
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], cl2e, mneg));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cl2e, mneg));
-          ps[e] += p0 + p1;
-          w[e] = pack_bf16(p0, p1);
-          prs[e] = add_bf16_pair(w[e], prs[e]);
-        }
-        pf[kb][t] = as_bf16x8(w);
-      }
-    l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
-    // O~^T += V_j^T P~_j^T (independent accumulators back to back)
-    if constexpr (D > 128) read_va();
-#pragma unroll
-    for (int kb = 0; kb < L::NKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
-    if constexpr (D > 128) sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
-    wait_vmem_all();
-    __syncthreads();
-  };
 
-  if constexpr (MASKED) {
-    for (int j = j0; j < ntile;) {
-      int jn = next_tile(j + 1);
-      step(j, jn, std::integral_constant<int, 0>{});
-      j = jn;
-      if (j >= ntile) break;
-      jn = next_tile(j + 1);
-      step(j, jn, std::integral_constant<int, 1>{});
-      j = jn;
+    if constexpr (MASKED) {
+      for (int j = j0; j < ntile;) {
+        int jn = next_tile(j + 1);
+        step(j, jn, std::integral_constant<int, 0>{});
+        j = jn;
+        if (j >= ntile) break;
+        jn = next_tile(j + 1);
+        step(j, jn, std::integral_constant<int, 1>{});
+        j = jn;
+      }
+    } else {
+      for (int j = j0; j < ntile; j += 2) {
+        step(j, j + 1, std::integral_constant<int, 0>{});
+        if (j + 1 < ntile) step(j + 1, j + 2, std::integral_constant<int, 1>{});
+      }
     }
-  } else {
-    for (int j = j0; j < ntile; j += 2) {
-      step(j, j + 1, std::integral_constant<int, 0>{});
-      if (j + 1 < ntile) step(j + 1, j + 2, std::integral_constant<int, 1>{});
-    }
+
+    if (qw >= Tq) continue;
+    const float l_tot = half_swap_sum(l_part);
+    const float lr_tot = half_swap_sum(lr_part);
+    if (myq >= Tq) continue;
+    // a row that sees no key (possible only under a block mask or a band) gets O = 0, lse = -inf
+    const float inv = (!(MASKED || BAND != 0) || lr_tot > 0.f) ? 1.f / lr_tot : 0.f;
+#pragma unroll
+    for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hf;
+        const size_t off = qbase + (size_t)myq * D + d0;
+        if (OUT_F32) {
+          const f32x4 w = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(O) + off) = w;
+        } else {
+          u32x2 w;
+          w[0] = pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+          w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+          st8(static_cast<uint16_t*>(O) + off, w);
+        }
+      }
+    if (hf == 0)
+      lse[(size_t)bh * Tq + myq] = (!(MASKED || BAND != 0) || l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   }
-
-  if (qw >= Tq) return;
-  const float l_tot = half_swap_sum(l_part);
-  const float lr_tot = half_swap_sum(lr_part);
-  if (myq >= Tq) return;
-  // a row that sees no key (possible only under a block mask or a band) gets O = 0, lse = -inf
-  const float inv = (!(MASKED || BAND != 0) || lr_tot > 0.f) ? 1.f / lr_tot : 0.f;
-#pragma unroll
-  for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = db * 32 + 8 * g + 4 * hf;
-      const size_t off = qbase + (size_t)myq * D + d0;
-      if (OUT_F32) {
-        const f32x4 w = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
-        *reinterpret_cast<f32x4*>(static_cast<float*>(O) + off) = w;
-      } else {
-        u32x2 w;
-        w[0] = pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        st8(static_cast<uint16_t*>(O) + off, w);
-      }
-    }
-  if (hf == 0)
-    lse[(size_t)bh * Tq + myq] = (!(MASKED || BAND != 0) || l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL, bool OUT_F32, bool MASKED, int BAND>
@@ -476,7 +490,10 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int
   } else if (bmask) {
     launch_dtype<D, true>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
   } else {
-    launch_dtype<D, false>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk);
+    // plain causal: query blocks nqb-1-p and p share a workgroup
+    const dim3 pgrid((unsigned)((long long)((nqb + 1) / 2) * B * H));
+    launch_dtype<D, false>(causal ? pgrid : grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb,
+                           nullptr, H, 0, nmk);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
