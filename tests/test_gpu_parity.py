@@ -41,7 +41,9 @@ def test_forward_parity(dtype, d, Tq, Tk, causal):
 
 @pytest.mark.parametrize("dtype,grad", [("bf16", "bf16"), ("bf16", "f32"), ("bf16", "f32o"), ("f32", "f32")])
 @pytest.mark.parametrize("d", DIMS)
-@pytest.mark.parametrize("Tq,Tk", [(1, 1), (17, 17), (100, 100), (300, 300), (100, 257), (257, 100)])
+# 700: an odd number of 256-query dQ blocks and an even number of 128-key blocks
+# (causal workgroups take two blocks each; with an odd count the middle one runs alone)
+@pytest.mark.parametrize("Tq,Tk", [(1, 1), (17, 17), (100, 100), (300, 300), (700, 700), (100, 257), (257, 100)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_parity(dtype, grad, d, Tq, Tk, causal):
     t = torch()
