@@ -31,9 +31,9 @@
 // you never visit": the sweep stops at the block's last query).
 //
 // One barrier per block: block j's S, softmax and PV run while K_{j+1} and
-// V_{j+1} are in flight from HBM into the other LDS stage.  On gfx950 the MFMA and vector-ALU
-// work of a SIMD do not overlap in time (the second wave on the SIMD covers
-// latencies), so the softmax is kept to as few vector instructions per score
+// V_{j+1} are in flight from HBM into the other LDS stage.  On gfx950 the MFMA
+// and vector-ALU work of a SIMD overlap only in part, within a wave and across
+// its two waves, so the softmax is kept to as few vector instructions per score
 // as possible.
 // Epilogue ([ZtF] step 3): O = O~/l (bf16 or float32), lse = ln2 (m + log2 l).
 #include <type_traits>
