@@ -14,6 +14,10 @@
 //     bwd_kv_w4_kernel for d = 256);
 //   * query-block sweep (bwd_dq_kernel): one workgroup per block of queries
 //     sweeps the key blocks and writes dQ_i once.
+// Under a plain causal mask a workgroup runs two blocks in turn, a short sweep
+// and a long one, so that all workgroups are about equally long (the key-block
+// sweep does so at d = 128); workgroups of unequal length leave CUs idle,
+// waiting on the dispatcher.
 // The split forms S and dP twice (seven tile products instead of five) but
 // sends no dQ traffic beyond one write: adding each key block's share of dQ
 // with float32 atomics would send Tk/128 partial sums per dQ element through

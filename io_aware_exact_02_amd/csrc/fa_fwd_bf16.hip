@@ -4,7 +4,9 @@
 //
 // One workgroup owns a block of 128 query rows of one (batch, head) and makes
 // one sweep over the key/value blocks ([ZtF] "The forward pass"); each of its
-// four waves owns 32 query rows, held as MFMA B operands in registers.
+// four waves owns 32 query rows, held as MFMA B operands in registers.  Under a
+// plain causal mask a workgroup runs two blocks in turn, a short and a long one,
+// so that all workgroups sweep about the same number of key blocks.
 //
 // Data movement per key block j of BC keys:
 //   * K_j goes HBM -> LDS with buffer_load ... lds (no registers, no VALU):
