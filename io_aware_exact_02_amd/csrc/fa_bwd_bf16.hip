@@ -884,8 +884,8 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   __shared__ __attribute__((aligned(1024))) char stage1[L::STAGE];
   auto stage_ptr = [&](int st) -> char* { return st == 0 ? stage0 : stage1; };
 
-  // Plain causal: workgroup p of a head runs query block p, then block nqb-1-p
-  // (the short block first, as in the forward), so every workgroup sweeps about
+  // Plain causal: workgroup p of a head runs query block nqb-1-p, then block p
+  // (the long block first, as in the forward), so every workgroup sweeps about
   // the same number of key blocks (uneven workgroups leave CUs waiting on the
   // dispatcher).  Otherwise one block per
   // workgroup, causal sweeps longest first.
@@ -904,7 +904,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   // epilogue.  A block's last step ends on a barrier after all its LDS reads, so
   // the next block's first DMA cannot overwrite a tile still in use.
   for (int pass = 0; pass < npass; ++pass) {
-    const int qb = !CAUSAL ? pidx : (npass == 2 && pass == 0) ? pidx : nqb - 1 - pidx;
+    const int qb = !CAUSAL ? pidx : (npass == 2 && pass == 1) ? pidx : nqb - 1 - pidx;
     const int q0 = qb * L::BR;
     const int qw = q0 + wave * 32;
     const int myq = qw + lq;
@@ -1228,7 +1228,7 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
     }
   }
   if (phases & FA_BWD_POST) {
-    // plain causal: query blocks p and nqb-1-p share a workgroup
+    // plain causal: query blocks nqb-1-p and p share a workgroup
     const bool paired = causal && !bmask && band == 0;
     const long long ndq = paired ? (long long)((nqb + 1) / 2) * B * H : nqblk;
     auto dqk = [&](auto kernel) {

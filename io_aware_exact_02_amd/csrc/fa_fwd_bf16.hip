@@ -112,7 +112,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // different XCDs round-robin; remapping gives each XCD a contiguous range of
   // logical blocks, so one head's query blocks (which share K and V) run on
   // the same L2.
-  // Plain causal: workgroup p of a head runs query block p, then block nqb-1-p,
+  // Plain causal: workgroup p of a head runs query block nqb-1-p, then block p,
   // so every workgroup sweeps about the same number of key tiles.  With one
   // block each, lengths range from 1 to nqb blocks' worth, and the dispatcher
   // leaves CUs with a free slot idle for tens of microseconds at a time.
@@ -134,9 +134,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // epilogue.  A block's last step ends on a barrier after all its LDS reads, so
   // the next block's first DMA cannot overwrite a tile still in use.
   for (int pass = 0; pass < npass; ++pass) {
-    // the short block first: the long sweeps of a head's workgroups then start a
-    // few tiles apart and find its first K/V tiles still in L2
-    const int qb = (npass == 2 && pass == 0) ? pidx : nqb - 1 - pidx;
+    // the long block first: a head's workgroups start their long sweeps together
+    // and share each K/V tile in L2; the staggered sweeps are the short ones
+    const int qb = (npass == 2 && pass == 1) ? pidx : nqb - 1 - pidx;
     const int q0 = qb * kBR;
     const int qw = q0 + wave * 32;
     const int myq = qw + lq;
@@ -494,7 +494,7 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int
   } else if (bmask) {
     launch_dtype<D, true>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
   } else {
-    // plain causal: query blocks p and nqb-1-p share a workgroup
+    // plain causal: query blocks nqb-1-p and p share a workgroup
     const dim3 pgrid((unsigned)((long long)((nqb + 1) / 2) * B * H));
     launch_dtype<D, false>(causal ? pgrid : grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb,
                            nullptr, H, 0, nmk);
