@@ -24,7 +24,10 @@
 // exp2: P~ = exp2(S c - m) against a reference maximum m that is moved (and O~
 // and the sums rescaled by exp2(m_old - m_new)) only when a row's maximum has
 // grown past it by more than 8; in between, the same reference holds for
-// numerator and denominator, so the result is unchanged and P~ <= 2^8.
+// numerator and denominator, so the result is unchanged and P~ <= 2^8.  At
+// d = 64 and 256 the row maximum is formed only on tiles where some lane's
+// share of the tile's row sum exceeds 2^8: below that, no weight can, so no
+// score passed the reference by more than the slack.
 // Two running sums: the unrounded one gives lse; O~ is divided by the sum of
 // the bf16-rounded weights the PV product actually used, which cancels the
 // rounding of a row's dominant weight to first order.
@@ -54,6 +57,7 @@ template <> struct FwdCfg<256> { static constexpr int BC = 32; static constexpr 
 constexpr int kWaves = 4;
 constexpr int kBR = 32 * kWaves;     // query rows per workgroup
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr float kMaxWeight = 256.0f;   // 2^kRescaleSlack
 
 template <int D>
 struct FwdLayout {
@@ -313,9 +317,11 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       v_dma(first_row(jn), nxt + L::V_OFF);
       f32x16 s[L::NKB];
       s_product(s, cur + L::K_OFF);
-      // V^T operands of the PV product.  For d <= 128 they are read here, so that
-      // their latency hides behind the softmax; at d = 256 (one wave per SIMD, all
-      // registers in use) holding them that long costs more than it hides.
+      // V^T operands of the PV product.  At d = 128 they are read here, so that
+      // their latency hides behind the softmax.  At d = 64 and 256 they are read
+      // after it: there the registers go to the softmax's fast path (below), which
+      // saves more than the early reads did (at d = 256, with one wave per SIMD,
+      // holding them through the softmax costs more than it hides anyway).
       const char* vs = cur + L::V_OFF;
       bf16x8 va[L::NKB][2][L::NDB];
       auto read_va = [&]() {
@@ -330,71 +336,92 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
               va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
       };
-      if constexpr (D <= 128) read_va();
+      // fast path of the softmax: at d = 128 it spills or, with late V^T reads,
+      // gains nothing; at d = 64 and 256 it saves 2-5% of the forward
+      constexpr bool FAST = D != 128;
+      if constexpr (!FAST) read_va();
       mask_tile(s, j);
-      // row maximum and (below) row sums as shallow trees of independent partial
-      // results: long chains of dependent vector ops leave the wave stalled
-      float mq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // chain q folds s[kb][4q .. 4q+3] for every kb, two new values per max3
-        float m = max3f(s[0][4 * q], s[0][4 * q + 1], s[0][4 * q + 2]);
-        float pend = s[0][4 * q + 3];
-        bool has = true;
-#pragma unroll
-        for (int kb = 1; kb < L::NKB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (has) m = max3f(m, pend, s[kb][4 * q + e]);
-            else pend = s[kb][4 * q + e];
-            has = !has;
-          }
-        mq[q] = has ? max2f(m, pend) : m;
-      }
-      float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
-      mx = half_swap_max(mx) * cl2e;
-      const bool grow = mx > m_ref + kRescaleSlack;     // never true for a row with no visible key yet
-      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
-        const float alpha = grow ? fast_exp2(m_ref - mx) : 1.f;   // 0 on a row's first block
-        if (grow) m_ref = mx;
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        l_part *= alpha;
-        lr_part *= alpha;
-      }
-      const float mneg = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      // P~ rounded to bf16 for the PV product; both sums updated
+      // P~ rounded to bf16 for the PV product, and this lane's shares of both row sums
       bf16x8 pf[L::NKB][2];
-      float ps[4] = {0.f, 0.f, 0.f, 0.f}, prs[4] = {0.f, 0.f, 0.f, 0.f};
+      float ps[4], prs[4];
+      auto weights = [&](float mneg) {
 #pragma unroll
-      for (int kb = 0; kb < L::NKB; ++kb)
+        for (int e = 0; e < 4; ++e) ps[e] = prs[e] = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 w;
+        for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * t + 2 * e;
-            const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], cl2e, mneg));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cl2e, mneg));
-            ps[e] += p0 + p1;
-            w[e] = pack_bf16(p0, p1);
-            prs[e] = add_bf16_pair(w[e], prs[e]);
+          for (int t = 0; t < 2; ++t) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * t + 2 * e;
+              const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], cl2e, mneg));
+              const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], cl2e, mneg));
+              ps[e] += p0 + p1;
+              w[e] = pack_bf16(p0, p1);
+              prs[e] = add_bf16_pair(w[e], prs[e]);
+            }
+            pf[kb][t] = as_bf16x8(w);
           }
-          pf[kb][t] = as_bf16x8(w);
+      };
+      // Fast path: with the reference maximum kept, a lane's share of the tile's
+      // row sum bounds each weight it holds, so shares of at most 2^slack on every
+      // lane mean that no score passed the reference by more than the slack: no
+      // rescale is due and the row maximum is not needed.  Otherwise (a row's
+      // first block, a grown maximum, overflow, NaN) it is formed and the weights
+      // redone, with the same decisions as without the fast path.
+      bool need_max = !FAST || __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0ull;
+      if (!need_max) {
+        weights(-m_ref);
+        const float share = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        need_max = __builtin_amdgcn_ballot_w64(!(share <= kMaxWeight)) != 0ull;
+      }
+      if (need_max) {
+        // row maximum as shallow trees of independent partial results: long
+        // chains of dependent vector ops leave the wave stalled
+        float mq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // chain q folds s[kb][4q .. 4q+3] for every kb, two new values per max3
+          float m = max3f(s[0][4 * q], s[0][4 * q + 1], s[0][4 * q + 2]);
+          float pend = s[0][4 * q + 3];
+          bool has = true;
+#pragma unroll
+          for (int kb = 1; kb < L::NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (has) m = max3f(m, pend, s[kb][4 * q + e]);
+              else pend = s[kb][4 * q + e];
+              has = !has;
+            }
+          mq[q] = has ? max2f(m, pend) : m;
         }
+        float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
+        mx = half_swap_max(mx) * cl2e;
+        const bool grow = mx > m_ref + kRescaleSlack;     // never true for a row with no visible key yet
+        if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+          const float alpha = grow ? fast_exp2(m_ref - mx) : 1.f;   // 0 on a row's first block
+          if (grow) m_ref = mx;
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          l_part *= alpha;
+          lr_part *= alpha;
+        }
+        weights((m_ref == -INFINITY) ? 0.f : -m_ref);
+      }
       l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
       // O~^T += V_j^T P~_j^T (independent accumulators back to back)
-      if constexpr (D > 128) read_va();
+      if constexpr (FAST) read_va();
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
-      if constexpr (D > 128) sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
+      if constexpr (FAST) sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
       wait_vmem_all();
       __syncthreads();
     };
