@@ -1066,8 +1066,9 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
             dp = mfma32(va[ds], gf[ds], dp);
           }
           sched_reads_ahead<2 * L::NDS>();
-          // K^T operands of the dQ product for k-step t = 0, read now so that their
-          // latency hides behind the softmax (all of them at once would spill)
+          // K^T operands of the dQ product, read now so that their latency hides
+          // behind the softmax: both k-steps at d = 64, k-step t = 0 only at d = 128
+          // and 256 (all of them at once would spill there)
           const char* ks = stage_ptr(ST) + L::K_OFF + kb * 32 * L::RB;
           bf16x8 ta[2][L::NDB];
 #pragma unroll
@@ -1075,6 +1076,14 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
             const u32x2 lo = ld8_tr(ks + (tb[0] ^ (db << 6)));
             const u32x2 hi = ld8_tr(ks + (tb[1] ^ (db << 6)));
             ta[0][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          }
+          if constexpr (D == 64) {
+#pragma unroll
+            for (int db = 0; db < L::NDB; ++db) {
+              const u32x2 lo = ld8_tr(ks + 16 * L::RB + (tb[0] ^ (db << 6)));
+              const u32x2 hi = ld8_tr(ks + 16 * L::RB + (tb[1] ^ (db << 6)));
+              ta[1][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
           }
           float p[16];
 #pragma unroll
@@ -1097,13 +1106,15 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
             }
             sf[t] = as_bf16x8(w);
           }
-          // dQ^T += K_j^T dS^T: lane = query column, register = feature row (the
-          // operands of k-step t = 1 are read here)
+          // dQ^T += K_j^T dS^T: lane = query column, register = feature row (at
+          // d = 128 and 256 the operands of k-step t = 1 are read here)
+          if constexpr (D != 64) {
 #pragma unroll
-          for (int db = 0; db < L::NDB; ++db) {
-            const u32x2 lo = ld8_tr(ks + 16 * L::RB + (tb[0] ^ (db << 6)));
-            const u32x2 hi = ld8_tr(ks + 16 * L::RB + (tb[1] ^ (db << 6)));
-            ta[1][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            for (int db = 0; db < L::NDB; ++db) {
+              const u32x2 lo = ld8_tr(ks + 16 * L::RB + (tb[0] ^ (db << 6)));
+              const u32x2 hi = ld8_tr(ks + 16 * L::RB + (tb[1] ^ (db << 6)));
+              ta[1][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
           }
 #pragma unroll
           for (int t = 0; t < 2; ++t)
