@@ -12,7 +12,9 @@ from tests.gpu_util import TOL_GRAD, TOL_LSE, TOL_O, draw, maxabs, to_dev, to_f6
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1, 1), (17, 17), (100, 100), (300, 300), (1000, 1000), (100, 257), (257, 100), (64, 513)]
+# causal workgroups take a short and a long block each: 200 gives two 128-row blocks (one
+# workgroup runs both), 300 three (the middle one alone), 1000 eight
+SHAPES = [(1, 1), (17, 17), (100, 100), (200, 200), (300, 300), (1000, 1000), (100, 257), (257, 100), (64, 513)]
 DIMS = [64, 128, 256]
 
 
@@ -41,9 +43,11 @@ def test_forward_parity(dtype, d, Tq, Tk, causal):
 
 @pytest.mark.parametrize("dtype,grad", [("bf16", "bf16"), ("bf16", "f32"), ("bf16", "f32o"), ("f32", "f32")])
 @pytest.mark.parametrize("d", DIMS)
-# 700: an odd number of 256-query dQ blocks and an even number of 128-key blocks
-# (causal workgroups take two blocks each; with an odd count the middle one runs alone)
-@pytest.mark.parametrize("Tq,Tk", [(1, 1), (17, 17), (100, 100), (300, 300), (700, 700), (100, 257), (257, 100)])
+# 700: an odd number of 256-query dQ blocks and an even number of 128-key blocks; 200: two
+# 128-key blocks in one workgroup (causal workgroups take two blocks each; with an odd count
+# the middle one runs alone)
+@pytest.mark.parametrize("Tq,Tk", [(1, 1), (17, 17), (100, 100), (200, 200), (300, 300), (700, 700), (100, 257),
+                                   (257, 100)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_parity(dtype, grad, d, Tq, Tk, causal):
     t = torch()
