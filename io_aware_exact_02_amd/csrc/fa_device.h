@@ -120,20 +120,22 @@ __device__ __forceinline__ float add_bf16_pair(unsigned pair, float acc) {
 }
 
 // Scheduling hint for a block of LDS operand reads feeding MFMAs, written
-// reads-first: keep the first reads six MFMAs ahead, then issue one read per
-// MFMA.  Without it the scheduler issues each read just before its MFMA, so
-// every MFMA pair waits out a full LDS round trip.
-// With R reads and M MFMAs (R >= M) the first R - M + 6 reads go ahead.
-template <int M, int R = M>
+// reads-first: keep the first reads A MFMAs ahead (six by default), then issue
+// one read per MFMA.  Without it the scheduler issues each read just before its
+// MFMA, so every MFMA pair waits out a full LDS round trip.
+// With R reads and M MFMAs (R >= M) the first R - M + A reads go ahead; A is
+// capped at M (all reads first).
+template <int M, int R = M, int A0 = 6>
 __device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int A = A0 < M ? A0 : M;
   static_assert(M >= 6 && R >= M, "at least six MFMAs, no fewer reads than MFMAs");
-  __builtin_amdgcn_sched_group_barrier(0x100, R - M + 6, 0);   // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, R - M + A, 0);   // DS reads
 #pragma unroll
-  for (int i = 0; i < M - 6; ++i) {
+  for (int i = 0; i < M - A; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
 }
 
 // Bits 64w .. 64w+63 of a byte mask, as one 64-bit word that is the same in
