@@ -54,7 +54,9 @@ typedef enum {
   FA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than fa_bwd_workspace_bytes */
   FA_ERR_LAUNCH = -7,     /* the HIP runtime rejected a launch                   */
   FA_ERR_ALIGN = -8,      /* a device pointer is not 16-byte aligned             */
-  FA_ERR_PHASE = -9       /* unknown bits in an fa_bwd_phases mask               */
+  FA_ERR_PHASE = -9,      /* unknown bits in an fa_bwd_phases mask               */
+  FA_ERR_SCRATCH = -10    /* fa_bwd_noalloc: the problem needs more than the
+                             library's fixed scratch (FA_NOALLOC_SCRATCH_BYTES)  */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -127,6 +129,28 @@ int fa_bwd_phases(const void* Q, const void* K, const void* V, const void* O, co
                   int B, int H, int Tq, int Tk, int d, float scale, int causal,
                   int dtype, int o_dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
                   int phases, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): fa_bwd with
+ * no workspace argument.  Its workspace is a fixed array inside the library,
+ * FA_NOALLOC_SCRATCH_BYTES long (16 MiB: fa_bwd_workspace_bytes up to that
+ * size, i.e. B*H*Tq up to 2^21 query rows for bfloat16 inputs and 2^22 for
+ * float32), one copy per GPU, held until the process ends.  The call
+ * allocates nothing; its first call on a device looks up that device's copy
+ * (with the device current).  Arguments, layouts, outputs and errors as fa_bwd,
+ * on the current device's stream `stream`, plus FA_ERR_SCRATCH when
+ * fa_bwd_workspace_bytes(...) exceeds FA_NOALLOC_SCRATCH_BYTES (checked before
+ * any device work) and FA_ERR_LAUNCH if the runtime cannot provide the
+ * array's address.  Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (two streams, two host threads) race.  The array's
+ * contents on entry do not matter (each call writes what it reads).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* lse, void* dQ, void* dK, void* dV,
+                   int B, int H, int Tq, int Tk, int d, float scale, int causal,
+                   int dtype, int o_dtype, int grad_dtype, void* stream);
 
 /*
  * Split-key forward for few query rows per head (decoding) -- the same

@@ -25,7 +25,8 @@ __all__ = [
     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "forward_splitkv", "fa_fwd_masked", "fa_bwd_masked",
     "fa_bwd_masked_phases", "forward_masked", "backward_masked", "MASK_BLOCK", "fa_fwd_window", "fa_bwd_window",
     "fa_bwd_window_phases", "forward_window", "backward_window", "fa_fwd_docs", "fa_bwd_docs",
-    "fa_bwd_docs_phases", "forward_docs", "backward_docs", "EXPORTED_SYMBOLS",
+    "fa_bwd_docs_phases", "forward_docs", "backward_docs", "EXPORTED_SYMBOLS", "fa_bwd_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 FA_F32 = 0
@@ -34,7 +35,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_bwd", "fa_bwd_phases", "fa_bwd_workspace_bytes", "fa_strerror",
                     "fa_abi_version", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_masked",
                     "fa_bwd_masked", "fa_bwd_masked_phases", "fa_fwd_window", "fa_bwd_window",
-                    "fa_bwd_window_phases", "fa_fwd_docs", "fa_bwd_docs", "fa_bwd_docs_phases")
+                    "fa_bwd_window_phases", "fa_fwd_docs", "fa_bwd_docs", "fa_bwd_docs_phases",
+                    "fa_bwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20   # FA_NOALLOC_SCRATCH_BYTES: fa_bwd_noalloc's fixed workspace
 MASK_BLOCK = 128          # block-mask granularity, in query rows and in keys
 FA_BWD_PRE, FA_BWD_MAIN, FA_BWD_POST, FA_BWD_ALL = 1, 2, 4, 7
 
@@ -90,6 +93,8 @@ def library() -> ctypes.CDLL:
     lib.fa_bwd_docs.restype = i
     lib.fa_bwd_docs_phases.argtypes = lib.fa_bwd_docs.argtypes[:-1] + [i, vp]
     lib.fa_bwd_docs_phases.restype = i
+    lib.fa_bwd_noalloc.argtypes = lib.fa_bwd.argtypes[:19] + [vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     _lib = lib
@@ -226,6 +231,32 @@ def fa_bwd_phases(q, k, v, o, do, lse, dq, dk, dv, workspace, phases, *, scale=N
                                  int(phases), _stream_handle(stream, dev))
     if st != 0:
         raise FAError(st, "fa_bwd_phases")
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, *, scale=None, causal=False, stream=None) -> None:
+    """The backward pass with no workspace argument (fa_bwd_noalloc): the library's
+    fixed per-GPU scratch holds the row terms, so the call allocates nothing.
+    Problems whose workspace would exceed NOALLOC_SCRATCH_BYTES raise FAError
+    (FA_ERR_SCRATCH); calls that overlap on one GPU race on the shared scratch."""
+    torch = _torch()
+    B, H, Tq, d = q.shape
+    Tk = k.shape[2]
+    dev = q.device
+    _check(q, "q", (B, H, Tq, d), device=dev)
+    for name, t, T in (("k", k, Tk), ("v", v, Tk), ("do", do, Tq)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    _check(o, "o", (B, H, Tq, d), None, dev)
+    _check(lse, "lse", (B, H, Tq), torch.float32, dev)
+    _check(dq, "dq", (B, H, Tq, d), None, dev)
+    _check(dk, "dk", (B, H, Tk, d), dq.dtype, dev)
+    _check(dv, "dv", (B, H, Tk, d), dq.dtype, dev)
+    c = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = library().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Tq, Tk, d, c,
+                                  int(bool(causal)), _dtype_code(q), _dtype_code(o), _dtype_code(dq),
+                                  _stream_handle(stream, dev))
+    if st != 0:
+        raise FAError(st, "fa_bwd_noalloc")
 
 
 def _check_mask(block_mask, H, Tq, Tk, dev):

@@ -69,6 +69,25 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
 
 }  // namespace
 
+namespace fa {
+
+// The checks of fa_bwd that do not involve the workspace, in the same order.
+int check_bwd_args(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                   void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int dtype,
+                   int o_dtype, int grad_dtype) {
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return FA_ERR_NULL;
+  int st = check_common(B, H, Tq, Tk, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!valid_dtype(grad_dtype) || (dtype == FA_F32 && grad_dtype != FA_F32)) return FA_ERR_DTYPE;
+  if (!valid_dtype(o_dtype) || (dtype == FA_F32 && o_dtype != FA_F32)) return FA_ERR_DTYPE;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_abi_version(void) { return 1; }
@@ -85,6 +104,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
     case FA_ERR_PHASE: return "unknown bits in the backward phase mask";
+    case FA_ERR_SCRATCH: return "problem too large for the library's static scratch (fa_bwd_noalloc)";
     default: return "unknown fa_status";
   }
 }

@@ -9,6 +9,12 @@ namespace fa {
 // 64 floats (256 bytes), then (bf16 gradients only) the float32 dQ accumulator.
 inline long long bwd_rows_padded(long long rows) { return (rows + 63) / 64 * 64; }
 
+// fa_bwd's argument checks that do not involve the workspace (null pointers,
+// shape, head width, dtypes, scale, 16-byte alignment), in fa_bwd's order.
+int check_bwd_args(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse,
+                   void* dQ, void* dK, void* dV, int B, int H, int Tq, int Tk, int d, float scale, int dtype,
+                   int o_dtype, int grad_dtype);
+
 // bmask: optional block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)] (uint8, device memory)
 // band 1: sliding window, key l visible from query r iff r - wl <= l <= r + wr
 // (wl, wr >= 0; an unbounded side is passed as a large value).  band 2:

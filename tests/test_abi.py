@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
 OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN, PHASE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+SCRATCH = -10
 P = 0x10000          # a fake, 16-byte aligned pointer value: never dereferenced on these paths
 
 
@@ -41,13 +42,15 @@ def test_header_documents_every_status_code():
     text = open(HEADER).read()
     for name, val in (("FA_OK", 0), ("FA_ERR_NULL", -1), ("FA_ERR_SHAPE", -2), ("FA_ERR_HEADDIM", -3),
                       ("FA_ERR_DTYPE", -4), ("FA_ERR_SCALE", -5), ("FA_ERR_WORKSPACE", -6),
-                      ("FA_ERR_LAUNCH", -7), ("FA_ERR_ALIGN", -8), ("FA_ERR_PHASE", -9)):
+                      ("FA_ERR_LAUNCH", -7), ("FA_ERR_ALIGN", -8), ("FA_ERR_PHASE", -9),
+                      ("FA_ERR_SCRATCH", -10)):
         assert re.search(rf"{name}\s*=\s*{val}\b", text), name
 
 
 def test_strerror_and_version(lib):
     assert fa.fa_abi_version() == 1
-    msgs = {s: fa.fa_strerror(s) for s in (OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN, PHASE)}
+    msgs = {s: fa.fa_strerror(s) for s in (OK, NULL, SHAPE, HEADDIM, DTYPE, SCALE, WORKSPACE, LAUNCH, ALIGN, PHASE,
+                                           SCRATCH)}
     assert msgs[OK] == "success"
     assert len(set(msgs.values())) == len(msgs)
     assert "unknown" in fa.fa_strerror(12345)
@@ -259,3 +262,36 @@ def test_docs_argument_errors(lib):
     assert bwd(ws=None) == WORKSPACE
     assert bwd(phases=8) == PHASE
     assert bwd(phases=0) == OK              # checks only, launches nothing
+
+
+def _bwd_noalloc(lib, B=1, H=1, Tq=8, Tk=8, d=64, scale=0.125, dtype=fa.FA_BF16, gdtype=fa.FA_BF16, odtype=None,
+                 null_at=None, misalign_at=None):
+    ptrs = [P] * 9
+    if null_at is not None:
+        ptrs[null_at] = None
+    if misalign_at is not None:
+        ptrs[misalign_at] = P + 8
+    odtype = dtype if odtype is None else odtype
+    return lib.fa_bwd_noalloc(*ptrs, B, H, Tq, Tk, d, scale, 0, dtype, odtype, gdtype, None)
+
+
+def test_bwd_noalloc_argument_errors(lib):
+    """fa_bwd_noalloc checks its arguments as fa_bwd does, and rejects problems whose
+    workspace exceeds the fixed scratch with FA_ERR_SCRATCH, all before any HIP call."""
+    for i in range(9):
+        assert _bwd_noalloc(lib, null_at=i) == NULL, i
+        assert _bwd_noalloc(lib, misalign_at=i) == ALIGN, i
+    assert _bwd_noalloc(lib, B=0) == SHAPE
+    assert _bwd_noalloc(lib, d=48) == HEADDIM
+    assert _bwd_noalloc(lib, dtype=fa.FA_F32, gdtype=fa.FA_BF16) == DTYPE
+    assert _bwd_noalloc(lib, odtype=7) == DTYPE
+    assert _bwd_noalloc(lib, scale=0.0) == SCALE
+    # bf16: 8 bytes per (padded) query row; the scratch holds 2^21 rows
+    rows_max = fa.NOALLOC_SCRATCH_BYTES // 8
+    assert fa.fa_bwd_workspace_bytes(1, 32, rows_max // 32, 64, 128, fa.FA_BF16, fa.FA_BF16) \
+        == fa.NOALLOC_SCRATCH_BYTES
+    assert _bwd_noalloc(lib, B=1, H=32, Tq=rows_max // 32 + 1, Tk=64, d=128) == SCRATCH
+    assert _bwd_noalloc(lib, B=2, H=32, Tq=rows_max // 32, Tk=64, d=128) == SCRATCH
+    # float32: 4 bytes per row, twice the rows
+    assert _bwd_noalloc(lib, B=1, H=64, Tq=rows_max // 32 + 64, Tk=64, d=64, dtype=fa.FA_F32,
+                        gdtype=fa.FA_F32) == SCRATCH
