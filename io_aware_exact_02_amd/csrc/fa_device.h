@@ -83,6 +83,10 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A value the whole wave holds alike, as a scalar register (v_readfirstlane).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima): every vector
 // memory load issued so far has returned.  Placed where a loop iteration has
 // already consumed its loads, it tells the compiler's wait-count tracking that

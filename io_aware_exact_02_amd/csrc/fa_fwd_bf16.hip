@@ -24,10 +24,10 @@
 // exp2: P~ = exp2(S c - m) against a reference maximum m that is moved (and O~
 // and the sums rescaled by exp2(m_old - m_new)) only when a row's maximum has
 // grown past it by more than 8; in between, the same reference holds for
-// numerator and denominator, so the result is unchanged and P~ <= 2^8.  At
-// d = 64 and 256 the row maximum is formed only on tiles where some lane's
-// share of the tile's row sum exceeds 2^8: below that, no weight can, so no
-// score passed the reference by more than the slack.
+// numerator and denominator, so the result is unchanged and P~ <= 2^8.  The
+// row maximum is formed only on tiles where some lane's share of the tile's
+// row sum exceeds 2^8: below that, no weight can, so no score passed the
+// reference by more than the slack.
 // Two running sums: the unrounded one gives lse; O~ is divided by the sum of
 // the bf16-rounded weights the PV product actually used, which cancels the
 // rounding of a row's dominant weight to first order.
@@ -130,7 +130,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int pidx = lin % npb;
   const int npass = (PAIRED && 2 * pidx + 1 < nqb) ? 2 : 1;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, hf = lane >> 5;
   const size_t qbase = (size_t)bh * Tq * D;
   const size_t kbase = (size_t)bh * Tk * D;
@@ -145,10 +145,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int qw = q0 + wave * 32;
     const int myq = qw + lq;
 
-    // Per-head buffer resources: rows past Tq / Tk read as zeros.
+    // Buffer resource over the head's Q: rows past Tq read as zeros.
     const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
-    const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
-    const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
 
     // Q fragments (B operand of S^T = K Q^T): column = query, k = features.
     bf16x8 qf[L::NDS];
@@ -172,31 +170,31 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       jfirst = max(0, band.lo(q0)) / BC;
     }
 
-    // ---- K and V: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i.
-    auto k_dma = [&](int k0, char* kst) {
+    // ---- K and V: HBM -> LDS, swizzled.  Wave w issues DMA instructions g = w*KDMA_W + i;
+    // lane l of instruction g moves chunk s = 64 g + l of the tile: row s / NC, stored
+    // chunk s % NC, which holds source chunk (s % NC) ^ swizzle(row).  The lane offsets
+    // within a tile do not change between tiles; the tile's start goes into a buffer
+    // resource over rows k0 .. Tk-1 (scalar work only), so rows past Tk -- and whole
+    // tiles past the end -- read as zeros, and the wave index (a scalar) gives the
+    // LDS destination without vector instructions.
+    unsigned koff[L::KDMA_W], voff[L::KDMA_W];
 #pragma unroll
-      for (int i = 0; i < L::KDMA_W; ++i) {
-        const int g = wave * L::KDMA_W + i;
-        const int s = g * 64 + lane;
-        const int row = s / L::NC, cp = s % L::NC;
-        const int src = cp ^ kswz<L::NC>(row);
-        const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(kst + g * 1024), 16, off, 0, 0, 0);
-      }
-    };
-    auto v_dma = [&](int k0, char* vst) {
+    for (int i = 0; i < L::KDMA_W; ++i) {
+      const int s = (wave * L::KDMA_W + i) * 64 + lane;
+      const int row = s / L::NC, cp = s % L::NC;
+      koff[i] = (unsigned)(row * D + (cp ^ kswz<L::NC>(row)) * 8) * 2u;
+      voff[i] = (unsigned)(row * D + (cp ^ vswz<L::NC>(row)) * 8) * 2u;
+    }
+    auto tile_dma = [&](const uint16_t* base, int k0, char* dst, const unsigned* off) {
+      const int rows = Tk - k0;
+      const rsrc_t r = make_rsrc(base + kbase + (size_t)(k0 < Tk ? k0 : 0) * D, rows > 0 ? (unsigned)rows * D * 2u : 0u);
 #pragma unroll
-      for (int i = 0; i < L::KDMA_W; ++i) {
-        const int g = wave * L::KDMA_W + i;
-        const int s = g * 64 + lane;
-        const int row = s / L::NC, cp = s % L::NC;
-        const int src = cp ^ vswz<L::NC>(row);
-        const unsigned off = ((unsigned)(k0 + row) * D + src * 8) * 2u;
+      for (int i = 0; i < L::KDMA_W; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(vst + g * 1024), 16, off, 0, 0, 0);
-      }
+            r, (__attribute__((address_space(3))) void*)(dst + (wave * L::KDMA_W + i) * 1024), 16, off[i], 0, 0, 0);
     };
+    auto k_dma = [&](int k0, char* kst) { tile_dma(K, k0, kst, koff); };
+    auto v_dma = [&](int k0, char* vst) { tile_dma(V, k0, vst, voff); };
     // Per-lane K read offset (bytes, relative to a stage and a 32-key block) for
     // k-step ds: chunk (2 ds + hf) ^ swz of row lq.  The XOR only touches bits 5..7
     // of kbase_lane (rows are >= 128 bytes), so each k-step is kbase_lane ^ (ds << 5).
@@ -254,12 +252,20 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         return;
       }
       if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk)) {
+        // key k0 + c of register (kb, r) is masked iff c > lim, where c = 32 kb +
+        // 8 (r / 4) + r % 4 + 4 hf and lim is the lane's last visible key - k0; the
+        // sign of lim - c selects -inf by a bitfield insert (no per-score condition
+        // registers)
+        int lim = Tk - 1 - k0;
+        if (CAUSAL) lim = min(lim, myq - k0);
+        lim -= 4 * hf;
 #pragma unroll
         for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= Tk || (CAUSAL && key > myq)) s[kb][r] = -INFINITY;
+            const unsigned m = (unsigned)((lim - (kb * 32 + 8 * (r >> 2) + (r & 3))) >> 31);   // all ones iff masked
+            const float x = s[kb][r];   // a scalar copy: bit_cast of a vector element in place reads element 0
+            s[kb][r] = __builtin_bit_cast(float, (m & 0xff800000u) | (~m & __builtin_bit_cast(unsigned, x)));
           }
       }
     };
@@ -318,10 +324,10 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       f32x16 s[L::NKB];
       s_product(s, cur + L::K_OFF);
       // V^T operands of the PV product.  At d = 128 they are read here, so that
-      // their latency hides behind the softmax.  At d = 64 and 256 they are read
-      // after it: there the registers go to the softmax's fast path (below), which
-      // saves more than the early reads did (at d = 256, with one wave per SIMD,
-      // holding them through the softmax costs more than it hides anyway).
+      // their latency hides behind the softmax (with the softmax's fast path below,
+      // 255 registers and no spill).  At d = 64 and 256 they are read after it: at
+      // d = 256, with one wave per SIMD, holding them through the softmax costs
+      // more than it hides.
       const char* vs = cur + L::V_OFF;
       bf16x8 va[L::NKB][2][L::NDB];
       auto read_va = [&]() {
@@ -336,17 +342,18 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
               va[kb][t][db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
       };
-      // fast path of the softmax: at d = 128 it spills or, with late V^T reads,
-      // gains nothing; at d = 64 and 256 it saves 2-5% of the forward
-      constexpr bool FAST = D != 128;
-      if constexpr (!FAST) read_va();
+      if constexpr (D == 128) read_va();
       mask_tile(s, j);
       // P~ rounded to bf16 for the PV product, and this lane's shares of both row sums
       bf16x8 pf[L::NKB][2];
       float ps[4], prs[4];
       auto weights = [&](float mneg) {
+        // -0 + x is x for every x, so the first additions into ps fold away
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ps[e] = prs[e] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          ps[e] = -0.f;
+          prs[e] = 0.f;
+        }
 #pragma unroll
         for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
@@ -370,7 +377,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       // rescale is due and the row maximum is not needed.  Otherwise (a row's
       // first block, a grown maximum, overflow, NaN) it is formed and the weights
       // redone, with the same decisions as without the fast path.
-      bool need_max = !FAST || __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0ull;
+      bool need_max = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0ull;
       if (!need_max) {
         weights(-m_ref);
         const float share = (ps[0] + ps[1]) + (ps[2] + ps[3]);
@@ -414,14 +421,14 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
       // O~^T += V_j^T P~_j^T (independent accumulators back to back)
-      if constexpr (FAST) read_va();
+      if constexpr (D != 128) read_va();
 #pragma unroll
       for (int kb = 0; kb < L::NKB; ++kb)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < L::NDB; ++db) o[db] = mfma32(va[kb][t][db], pf[kb][t], o[db]);
-      if constexpr (FAST) sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
+      if constexpr (D != 128) sched_reads_ahead<L::NKB * 2 * L::NDB, 2 * L::NKB * 2 * L::NDB>();
       wait_vmem_all();
       __syncthreads();
     };
