@@ -911,8 +911,6 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 
     const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
     const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
-    const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
-    const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
     const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
     const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
 
@@ -949,17 +947,29 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
       jfirst = max(0, band.lo(q0)) / BC;
     }
 
-    // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled
-    const rsrc_t rkv = wave < L::WAVES / 2 ? rk : rv;
+    // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled.  Lane l of DMA
+    // instruction g moves chunk s = 64 (g % KDMA) + l of the tile: row s / NC,
+    // stored chunk s % NC, which holds source chunk (s % NC) ^ swizzle(row).  The
+    // lane offsets do not change between tiles; the tile's start goes into a
+    // buffer resource over rows k0 .. Tk-1 (scalar work only), so rows past Tk --
+    // and whole tiles past the end -- read as zeros.
+    const uint16_t* const kv_src = wave < L::WAVES / 2 ? K : V;
+    unsigned kvoff[L::KDMA_W];
+#pragma unroll
+    for (int i = 0; i < L::KDMA_W; ++i) {
+      const int s = ((wave * L::KDMA_W + i) % L::KDMA) * 64 + lane;
+      const int row = s / L::NC, cp = s % L::NC;
+      kvoff[i] = (unsigned)(row * D + (cp ^ dq_swz<L::NC>(row)) * 8) * 2u;
+    }
+    const unsigned* const kvo = kvoff;   // (the host compiler drops a kernel whose lambdas index a captured array)
     auto kv_dma = [&](int k0, int st) {
+      const int rows = Tk - k0;
+      const rsrc_t r = make_rsrc(kv_src + kbase + (size_t)(k0 < Tk ? k0 : 0) * D, rows > 0 ? (unsigned)rows * D * 2u : 0u);
 #pragma unroll
       for (int i = 0; i < L::KDMA_W; ++i) {
         const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
-        const int s = (g % L::KDMA) * 64 + lane;
-        const int row = s / L::NC, cp = s % L::NC;
-        const unsigned off = ((unsigned)(k0 + row) * D + (cp ^ dq_swz<L::NC>(row)) * 8) * 2u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rkv, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, off, 0, 0, 0);
+            r, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, kvo[i], 0, 0, 0);
       }
     };
     // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
