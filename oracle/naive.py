@@ -54,15 +54,10 @@ import numpy as np
 
 __all__ = [
     "scores_head", "probs_head", "forward_head", "backward_head",
-    "forward", "backward", "default_scale", "block_allowed", "MASK_BLOCK", "dq_rows", "window_allowed", "doc_allowed",
+    "forward", "backward", "block_allowed", "MASK_BLOCK", "dq_rows", "dk_cols", "window_allowed", "doc_allowed",
 ]
 
 MASK_BLOCK = 128   # side of a block-mask block, in query rows and in keys
-
-
-def default_scale(d: int) -> float:
-    """c = 1/sqrt(d_k) ([ZtF] "The backward pass, derived", definition of c)."""
-    return 1.0 / math.sqrt(d)
 
 
 def _visible(Tk: int, rows: np.ndarray, causal: bool) -> np.ndarray | None:
@@ -194,6 +189,32 @@ def dq_rows(q, k, v, do, scale, causal, rows, block_mask=None, window=None, docs
     D = np.sum(do_r * O, axis=1)
     dS = P * (do_r @ v.T - D[:, None])
     return scale * (dS @ k)
+
+
+def dk_cols(q, k, v, do, scale, causal, cols, block_mask=None, window=None, docs=None, row_block=1024):
+    """dK[cols] of one head by the same chain rule ([ZtF] "The backward pass,
+    derived"): column l of dK = c dS[:, l]^T Q needs column l of P and of
+    dP = dO V^T for every query row, and D_r = dO_r . O_r, so it needs O and lse
+    of every row that sees key l.  They come from the definition row block by
+    row block (no T x T matrix is held), then only the sampled columns of P and
+    dP are formed.  Under the causal rule a row r sees key l only when l <= r,
+    so rows before the first sampled key add nothing and are not visited."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    cols = np.asarray(cols)
+    out = np.zeros((len(cols), q.shape[1]))
+    first = int(cols.min()) if causal and len(cols) else 0
+    for r0 in range(first, q.shape[0], row_block):
+        rows = np.arange(r0, min(r0 + row_block, q.shape[0]))
+        P, _ = probs_head(q, k, scale, causal, rows, block_mask, window, docs)    # P[rows, :]
+        O = P @ v
+        D = np.sum(do[rows] * O, axis=1)
+        Pc = P[:, cols]
+        dS = Pc * (do[rows] @ v[cols].T - D[:, None])
+        out += scale * (dS.T @ q[rows])
+    return out
 
 
 def _heads(B, H, heads):

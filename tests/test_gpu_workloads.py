@@ -112,8 +112,8 @@ def test_d256_backward_whole_heads_t4096():
 
 def test_causal_bf16_b1h24_t65536_d256_backward_sampled_rows():
     """The d = 256 backward at full size (24 heads x 65536): dQ on sampled rows against
-    the oracle (a dQ row needs only its own row of P, dP and D), and dV through an exact
-    identity: rows of P sum to 1, so sum_l dV_l = sum_r dO_r.  With P rounded to bf16
+    the oracle (a dQ row needs only its own row of P, dP and D), dK on sampled keys of
+    the sequence's tail, and dV through an exact identity: rows of P sum to 1, so sum_l dV_l = sum_r dO_r.  With P rounded to bf16
     before the dV product each row's weights sum to 1 within 2^-9, which bounds the
     difference by 2^-9 sum_r |dO_r| (plus float32 summation slack)."""
     t = torch()
@@ -132,6 +132,12 @@ def test_causal_bf16_b1h24_t65536_d256_backward_sampled_rows():
     do = f["do"]
     bound = (2.0 ** -9 + 1e-5) * np.abs(do).sum(axis=2) + 1e-3
     assert np.all(np.abs(dv_sum - do.sum(axis=2)) <= bound)
+    # dK on sampled keys: a key's column of dK needs D_r (hence O) of every row that
+    # sees it; keys in the last 2048 positions are seen by at most 2048 rows each
+    keys = np.unique(np.concatenate([[w.Tk - 2048, w.Tk - 1], rng.integers(w.Tk - 2048, w.Tk, 14)]))
+    for b, h in _heads(w, 2, 8):
+        ref = naive.dk_cols(f["q"][b, h], f["k"][b, h], f["v"][b, h], f["do"][b, h], scale, True, keys)
+        assert maxabs(to_f64(dK[b, h][keys]), ref) <= TOL_GRAD["bf16"], (b, h)
 
 
 def test_cross_bf16_b16h16_tq1024_tk8192_d128_forward_and_backward():
@@ -155,3 +161,40 @@ def test_cross_bf16_b16h16_tq1024_tk8192_d128_forward_and_backward():
     t.cuda.synchronize()
     _check_fwd_heads(w, f, O32, lse32, heads)
     _check_bwd_heads(w, f, dQ, dK, dV, heads)
+    del dQ, dK, dV, O32, lse32
+    _check_bwd_through_bf16_o(w, f, dev, O, lse, heads)
+
+
+def _check_bwd_through_bf16_o(w, f, dev, O, lse, heads):
+    """The same backward fed the bf16 O of the forward (and returning bf16 or float32
+    gradients), against a bound derived from the rounding of O.  Rounding O to
+    bf16 moves each element by at most 2^-8 of itself, so D_r = dO_r . O_r moves
+    by at most e_r = 2^-8 sum_k |dO_rk O_rk|.  D enters every dS_rl = P_rl (dP_rl -
+    D_r), so dQ_r moves by at most c e_r |(P K)_r| and dK_l by at most
+    c sum_r P_rl e_r |Q_r|, elementwise; dV does not depend on D.  The check is the
+    gradient tolerance plus that bound (plus, for bf16 gradients, their own
+    rounding of at most 2^-8 of the value)."""
+    t = torch()
+    c = 1 / math.sqrt(w.d)
+    u = 2.0 ** -8
+    tol = TOL_GRAD[w.dtype]
+    for gdt in (t.float32, t.bfloat16):
+        dQ, dK, dV = fa.backward(dev["q"], dev["k"], dev["v"], O, dev["do"], lse, causal=w.causal, grad_dtype=gdt)
+        t.cuda.synchronize()
+        out_u = u if gdt == t.bfloat16 else 0.0
+        worst = {"dQ": 0.0, "dK": 0.0, "dV": 0.0}
+        for b, h in heads:
+            q, k, v, do = (f[n][b, h] for n in ("q", "k", "v", "do"))
+            rQ, rK, rV, rO = naive.backward_head(q, k, v, do, c, w.causal)[:4]
+            P = naive.probs_head(q, k, c, w.causal)[0]
+            e = u * np.sum(np.abs(do * rO), axis=1)                      # bound on |dD_r|
+            bq = c * e[:, None] * np.abs(P @ k)
+            bk = c * (P.T @ (e[:, None] * np.abs(q)))
+            for got, ref, bnd, name in ((dQ, rQ, bq, "dQ"), (dK, rK, bk, "dK"), (dV, rV, 0.0, "dV")):
+                err = np.abs(to_f64(got[b, h]) - ref)
+                lim = tol + bnd
+                lim = lim + out_u * (np.abs(ref) + lim)
+                assert np.all(err <= lim), (name, str(gdt), b, h, float((err - lim).max()))
+                worst[name] = max(worst[name], float(err.max()))
+        print(f"cross-attention backward through bf16 O, {gdt} gradients: max abs errors {worst}", flush=True)
+        del dQ, dK, dV

@@ -154,7 +154,9 @@ def check_torch_sdpa(fwd, bwd):
     torch = pytest.importorskip("torch")
     F = torch.nn.functional
     for causal in (False, True):
-        for (Tq, Tk) in ((11, 11), (6, 13)) if not causal else ((11, 11),):
+        # causal with Tq != Tk too: torch's is_causal keeps key l <= query r (top-left),
+        # the alignment the library takes (both ways round)
+        for (Tq, Tk) in ((11, 11), (6, 13), (13, 6)):
             d = 8
             q, k, v, do = _rand((Tq, d), 40), _rand((Tk, d), 41), _rand((Tk, d), 42), _rand((Tq, d), 43)
             scale = 1.0 / math.sqrt(d) * 1.7
@@ -341,3 +343,30 @@ def test_dq_rows_by_finite_differences(causal):
     bm = np.array([[1]], np.uint8)
     full = naive.backward_head(q, k, v, do, c, causal, block_mask=bm)[0]
     assert np.allclose(naive.dq_rows(q, k, v, do, c, causal, rows, block_mask=bm), full[rows], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dk_cols_by_finite_differences(causal):
+    """dk_cols pinned by central differences of L = sum(O * dO) in k[l, j] (every row
+    of O that sees key l moves), and equal to the same columns of the whole-head
+    backward, with and without a block mask and in row blocks smaller than the head."""
+    rng = np.random.default_rng(91)
+    Tq, Tk, d, c = 23, 29, 5, 0.7
+    q, k, v, do = (rng.standard_normal(sh) for sh in ((Tq, d), (Tk, d), (Tk, d), (Tq, d)))
+    cols = np.array([0, 4, 17, 22, 28])
+    got = naive.dk_cols(q, k, v, do, c, causal, cols, row_block=7)
+    h = 1e-6
+    for i, l in enumerate(cols):
+        for j in range(d):
+            p, m = k.copy(), k.copy()
+            p[l, j] += h
+            m[l, j] -= h
+            fd = (_loss(naive.forward_head, q, p, v, do, c, causal) -
+                  _loss(naive.forward_head, q, m, v, do, c, causal)) / (2 * h)
+            assert abs(fd - got[i, j]) <= 1e-7 * (1 + abs(fd)), (l, j, fd, got[i, j])
+    full = naive.backward_head(q, k, v, do, c, causal)[1]
+    assert np.allclose(got, full[cols], atol=1e-13)
+    bm = np.array([[1]], np.uint8)
+    full_m = naive.backward_head(q, k, v, do, c, causal, block_mask=bm)[1]
+    assert np.allclose(naive.dk_cols(q, k, v, do, c, causal, cols, block_mask=bm, row_block=5), full_m[cols],
+                       atol=1e-13)
