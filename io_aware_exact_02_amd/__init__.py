@@ -293,7 +293,7 @@ def fa_fwd_masked(q, k, v, o, lse, block_mask, *, scale=None, causal=False, stre
 
 def fa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace, *, scale=None, causal=False,
                   stream=None) -> None:
-    """Block-sparse backward (bf16 inputs, d in {64, 128}) into caller-provided dq, dk, dv."""
+    """Block-sparse backward (bf16 inputs, d in {64, 128, 256}) into caller-provided dq, dk, dv."""
     fa_bwd_masked_phases(q, k, v, o, do, lse, dq, dk, dv, block_mask, workspace, FA_BWD_ALL, scale=scale,
                          causal=causal, stream=stream)
 
