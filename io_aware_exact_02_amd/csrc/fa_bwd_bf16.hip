@@ -222,15 +222,18 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   // ---- staging of one query tile (Q_i, dO_i, Ln_i, Dn_i) ----
   // Whole waves stage one tensor each (so the buffer resource they load through
   // is wave-uniform): WPT waves per tensor, one 8x8 block (8 query rows x 8
-  // features) per lane, features fastest across lanes so that a row-major store
-  // covers whole rows.  The top 32 threads also fetch Ln and Dn.  A tile index
-  // past the sweep maps to row Tq, whose loads return zeros.
+  // features) per lane, the four row groups of a feature group on consecutive
+  // lanes.  (With the feature group fastest, the 16 lanes of a transposed store
+  // fall on two 16-byte bank groups, eight lanes each; this order makes that
+  // two lanes per group, at the price of two per group on the row-major stores.)
+  // The top 32 threads also fetch Ln and Dn.  A tile index past the sweep maps
+  // to row Tq, whose loads return zeros.
   constexpr int WPT = (L::NBLK + 63) / 64;
   const bool is_g = wave >= WPT;
   const int tb = (wave % WPT) * 64 + lane;
   const bool tloader = wave < 2 * WPT && tb < L::NBLK;
   const rsrc_t rsrc_t_src = is_g ? rg : rq;
-  const int dgq = tb % (D / 8), rg8 = tb / (D / 8);
+  const int dgq = tb / (kBQ / 8), rg8 = tb % (kBQ / 8);
   const int rt = rg8 >> 1, rh = rg8 & 1;
   auto trow = [&](int i) { return 16 * rt + 4 * rh + (i < 4 ? i : 4 + i); };
   const bool sloader = tid >= 256 - kBQ;
