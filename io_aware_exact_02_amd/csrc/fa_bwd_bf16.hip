@@ -115,41 +115,72 @@ struct KeyBlockTiles {
 };
 
 // ---------------------------------------------------------------------------
+// Chunk swizzle of row r of a row-major bf16 tile held in LDS (16-byte chunk c
+// of row r is stored at chunk c ^ row_swz(r)), for two kinds of reads.  Row
+// reads (16 lanes = 16 consecutive rows, one 16-byte chunk each) need the
+// swizzle to be a permutation over any 16 rows (for 128-byte rows, two per
+// 256-byte bank cycle: over the row pairs).  Transposing reads (a half-wave = 4
+// consecutive rows x 4 chunks, 8 bytes per lane) need the four rows to spread
+// a chunk group over all bank groups: the row's position among the four moves
+// chunk bits 2-3 (for 128-byte rows, the odd row pair flips bit 2).  The
+// swizzle changes chunk bits >= 2 only through the row, so a 32-feature
+// block's offset is a XOR with (db << 6).
+// ---------------------------------------------------------------------------
+template <int NC>
+__device__ __forceinline__ int row_swz(int r) {
+  if constexpr (NC == 8) {
+    const int u = (r >> 1) & 7;
+    return u ^ ((u & 1) << 2);
+  } else {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Key-block sweep for d = 256 (bwd_kv_w4_kernel): dK_j and dV_j.
 //
 // Four waves, one per SIMD, each owning 32 keys: K_j, V_j (MFMA B operands)
 // and the float32 accumulators dK_j, dV_j stay in registers (the accumulators
 // alone take 256 per lane, so two waves per SIMD do not fit).  Per query tile
-// i of 32 rows, double-buffered in LDS:
-//   * Q_i and dO_i go HBM -> registers one tile ahead -> LDS twice: row-major
-//     for the products over features, and transposed (query order permuted to
-//     the MFMA k-slots) for the products over queries.  Ln_i and Dn_i (the
-//     negated row terms) go beside them.
+// i of 32 rows, in a ring of three LDS stages:
+//   * Q_i, dO_i, Ln_i and Dn_i (the negated row terms) go HBM -> LDS by
+//     buffer_load ... lds two tiles ahead, Q_i and dO_i rows chunk-swizzled
+//     (row_swz).  One row-major copy serves both kinds of product: row reads
+//     for those over features, transposing 8-byte reads (one feature per lane,
+//     queries in the k-slot order of the P and dS fragments) for those over
+//     queries.
 //   * S = Q_i K_j^T and dP = dO_i V_j^T with one key per lane; P = exp2(S c
 //     log2e + Ln_i) and dS = P (dP + Dn_i) ([ZtF] "The backward pass,
 //     derived", Observations 1-3); only tiles crossing the causal diagonal
 //     are masked.  Rows past Tq and keys past Tk read as zeros and add nothing.
 //   * dV_j += P^T dO_i and dK_j += dS^T Q_i with P and dS straight from
 //     registers.
+// The copies are issued in inline assembly, out of the compiler's sight: it
+// cannot tell the stages of one LDS array apart and would otherwise wait for
+// every copy in flight before each transposing read.  The kernel does its own
+// waiting: before the barrier that closes a step, each wave waits for its
+// copies of the next tile (the copies complete in issue order).
 // dQ comes from the query-block sweep below, as for the narrower heads.
 // ---------------------------------------------------------------------------
 template <int D>
 struct W4Layout {
-  static constexpr int NSTR = D + 8;            // row-major tiles (bf16 per row)
-  static constexpr int TSTR = kBQ + 8;          // transposed tiles: D rows of 32 queries
-  static constexpr int Q_N = 0;                 // byte offsets inside one stage
-  static constexpr int Q_T = Q_N + kBQ * NSTR * 2;
-  static constexpr int G_N = Q_T + D * TSTR * 2;
-  static constexpr int G_T = G_N + kBQ * NSTR * 2;
-  static constexpr int L_F = G_T + D * TSTR * 2;       // Ln [32]
-  static constexpr int D_F = L_F + kBQ * 4;            // Dn [32]
-  static constexpr int STAGE = D_F + kBQ * 4;
-  static constexpr int BYTES = 2 * STAGE;
+  static constexpr int NC = D / 8;              // 16-byte chunks per row
+  static constexpr int RB = D * 2;              // bytes per row
+  static constexpr int TB = kBQ * RB;           // one Q or dO tile
+  static constexpr int Q_OFF = 0;               // byte offsets inside one stage
+  static constexpr int G_OFF = TB;
+  static constexpr int L_OFF = 2 * TB;          // Ln: 64 floats (the second 32 unused)
+  static constexpr int D_OFF = L_OFF + 256;     // Dn: likewise
+  static constexpr int X_OFF = D_OFF + 256;     // waves 2 and 3 copy their row terms here, unused
+  static constexpr int STAGE = X_OFF + 512;
+  static constexpr int NSTAGE = 3;
+  static constexpr int BYTES = NSTAGE * STAGE;
   static constexpr int NDS = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int NBLK = (kBQ / 8) * (D / 8);     // 8x8 blocks per tensor tile
-  static_assert(STAGE % 16 == 0, "LDS regions must stay 16-byte aligned");
-  static_assert(2 * ((NBLK + 63) / 64) <= 4, "Q and dO staging waves fit in the workgroup");
+  static constexpr int DMA_W = TB / 1024 / 2;   // 1 KiB copies per wave and tensor (two waves per tensor)
+  static constexpr int COPIES = DMA_W + 1;      // copies a wave issues per tile
+  static_assert(NC >= 16, "row_swz of 16 or more chunks");
+  static_assert(STAGE % 1024 == 0 && COPIES <= 15, "stage alignment; vmcnt field");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -162,7 +193,7 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
                       int nkb, int grad_f32, const uint8_t* __restrict__ bmask, int H, long long mask_hstride,
                       int nmk, int wl, int wr, const int* __restrict__ cu, int nd, int bcausal) {
   using L = W4Layout<D>;
-  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   const int nblk = gridDim.x, wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
@@ -176,12 +207,8 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   const int kw0 = k0 + wave * kKeysPerWave;
   const int mykey = kw0 + l32;
 
-  const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
-  const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
   const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
   const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
-  const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
-  const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
 
   // K_j and V_j as B operands (column = key, k = features), held for the sweep.
   bf16x8 kf[L::NDS], vf[L::NDS];
@@ -219,76 +246,71 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   }
   const int n = tiles.count();                  // query tiles in the sweep
 
-  // ---- staging of one query tile (Q_i, dO_i, Ln_i, Dn_i) ----
-  // Whole waves stage one tensor each (so the buffer resource they load through
-  // is wave-uniform): WPT waves per tensor, one 8x8 block (8 query rows x 8
-  // features) per lane, the four row groups of a feature group on consecutive
-  // lanes.  (With the feature group fastest, the 16 lanes of a transposed store
-  // fall on two 16-byte bank groups, eight lanes each; this order makes that
-  // two lanes per group, at the price of two per group on the row-major stores.)
-  // The top 32 threads also fetch Ln and Dn.  A tile index past the sweep maps
-  // to row Tq, whose loads return zeros.
-  constexpr int WPT = (L::NBLK + 63) / 64;
-  const bool is_g = wave >= WPT;
-  const int tb = (wave % WPT) * 64 + lane;
-  const bool tloader = wave < 2 * WPT && tb < L::NBLK;
-  const rsrc_t rsrc_t_src = is_g ? rg : rq;
-  const int dgq = tb / (kBQ / 8), rg8 = tb % (kBQ / 8);
-  const int rt = rg8 >> 1, rh = rg8 & 1;
-  auto trow = [&](int i) { return 16 * rt + 4 * rh + (i < 4 ? i : 4 + i); };
-  const bool sloader = tid >= 256 - kBQ;
-  const int srow = tid - (256 - kBQ);
-  u32x4 stg[8];
-  float sl = 0.f, sd = 0.f;
+  // ---- copies of one query tile into a stage.  Waves 0-1 move Q_i, waves 2-3
+  // dO_i: lane l of copy g (0 .. 2 DMA_W - 1 over the tensor's two waves) moves
+  // chunk s = 64 g + l of the tile, row s / NC, stored at chunk s % NC, which
+  // holds source chunk (s % NC) ^ row_swz(row).  Wave 0 also copies Ln_i and
+  // wave 1 Dn_i (64 floats from the tile's first row); waves 2 and 3 make the
+  // same copies into an unused slot, so that every wave issues COPIES per tile.
+  // The lane offsets do not change between tiles; the tile's first row goes
+  // into a buffer resource over rows r0 .. Tq-1, so rows past Tq -- and whole
+  // tiles past the sweep, which start at row Tq -- read as zeros.
+  const bool is_g = wave >= 2;
+  const uint16_t* const src = is_g ? dO : Q;
+  unsigned coff[L::DMA_W];
+#pragma unroll
+  for (int i = 0; i < L::DMA_W; ++i) {
+    const int s = ((wave & 1) * L::DMA_W + i) * 64 + lane;
+    const int row = s / L::NC, cp = s % L::NC;
+    coff[i] = (unsigned)(row * D + (cp ^ row_swz<L::NC>(row)) * 8) * 2u;
+  }
+  const unsigned* const co = coff;   // (the host compiler drops a kernel whose lambdas index a captured array)
+  const float* const terms = ((wave & 1) ? Dn : Ln) + (size_t)bh * Tq;
+  const unsigned lds0 = (unsigned)(size_t)smem;
+  const unsigned t_dst = (wave & 1) ? L::D_OFF : L::L_OFF;
+  const unsigned x_dst = is_g ? L::X_OFF + 256 * (wave & 1) : t_dst;
+  const unsigned c_dst = (is_g ? L::G_OFF : L::Q_OFF) + (wave & 1) * L::DMA_W * 1024;
   auto tile_row = [&](int t) { return t < nqt ? t * kBQ : Tq; };
-  auto gload = [&](int r0) {
-    if (tloader) {
+  auto copy_tile = [&](int t, int st) {
+    const int r0 = tile_row(t);
+    const int rows = Tq - r0;
+    const unsigned base = lds0 + (unsigned)st * L::STAGE;
+    const u32x4 r = raw_rsrc(src + qbase + (size_t)(r0 < Tq ? r0 : 0) * D, rows > 0 ? (unsigned)rows * D * 2u : 0u);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) stg[i] = bload16(rsrc_t_src, ((unsigned)(r0 + trow(i)) * D + dgq * 8) * 2u);
-    }
-    if (sloader) {
-      sl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (r0 + srow) * 4, 0, 0));
-      sd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (r0 + srow) * 4, 0, 0));
-    }
-  };
-  auto lstore = [&](int st) {
-    char* base = smem + st * L::STAGE;
-    if (tloader) {
-      char* N = base + (is_g ? L::G_N : L::Q_N);
-      char* T = base + (is_g ? L::G_T : L::Q_T);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st16(N + (trow(i) * L::NSTR + dgq * 8) * 2, stg[i]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x4 even, odd;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          even[p] = lo_lo(stg[2 * p][w], stg[2 * p + 1][w]);
-          odd[p] = hi_hi(stg[2 * p][w], stg[2 * p + 1][w]);
-        }
-        st16(T + ((dgq * 8 + 2 * w) * L::TSTR + 16 * rt + 8 * rh) * 2, even);
-        st16(T + ((dgq * 8 + 2 * w + 1) * L::TSTR + 16 * rt + 8 * rh) * 2, odd);
-      }
-    }
-    if (sloader) {
-      reinterpret_cast<float*>(base + L::L_F)[srow] = sl;
-      reinterpret_cast<float*>(base + L::D_F)[srow] = sd;
-    }
+    for (int i = 0; i < L::DMA_W; ++i) dma16_unseen(r, co[i], base + c_dst + i * 1024);
+    const u32x4 rt = raw_rsrc(terms + (r0 < Tq ? r0 : 0), rows > 0 ? (unsigned)rows * 4u : 0u);
+    dma4_unseen(rt, (unsigned)lane * 4u, base + x_dst);
   };
 
-  int tc = tiles.next(it0);                     // the tile of the next step
-  gload(tile_row(tc));
-  lstore(0);
-  wait_vmem_all();
-  __syncthreads();
+  // this lane's row read for k-step ds: chunk (2 ds + hf) ^ swz of row l32
+  const int swz_l = row_swz<L::NC>(l32);
+  const int n_lane = l32 * L::RB + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
+  // transposing reads (B operands of the products over queries): lane l gets
+  // feature 32 db + l % 32, queries 16 t + 4 hf + 0..3 and 16 t + 8 + 4 hf +
+  // 0..3 of the tile -- the k-slot order of the P and dS fragments.  Each half
+  // comes from one read in which lane 16 g + 4 e + j addresses query row
+  // 4 (g / 2) + e (+ 8 for the second half) and features 16 (g % 2) + 4 j ..
+  // +3; tb[sec] is that offset for t = db = 0.
+  const int tg = lane >> 4, ti = lane & 15;
+  int tb[2];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec) {
+    const int row = 8 * sec + 4 * (tg >> 1) + (ti >> 2);
+    const int c = 2 * (tg & 1) + ((ti & 3) >> 1);
+    tb[sec] = row * L::RB + ((c ^ row_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
+  }
+  auto tr_operand = [&](const char* tile, int t, int db) {
+    const char* base = tile + t * 16 * L::RB;
+    const u32x2 lo = ld8_tr(base + (tb[0] ^ (db << 6)));
+    const u32x2 hi = ld8_tr(base + (tb[1] ^ (db << 6)));
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
 
-  // tile t in stage ST (the step's parity in the sweep); tn is the tile after it.
-  // One step per loop iteration with the stage as a run-time offset: two
-  // unrolled steps per iteration make the compiler spill the accumulators.
-  auto step = [&](int t, int tn, int ST) {
+  // tile t in stage st; tile tf is copied into stage sf (two steps ahead)
+  auto step = [&](int t, int st, int tf, int sf) {
+    copy_tile(tf, sf);
     const int r0 = t * kBQ;
-    const char* sb_ = smem + ST * L::STAGE;
-    gload(tile_row(tn));
+    const char* sb_ = smem + st * L::STAGE;
 
     // S = Q_i K_j^T and dP = dO_i V_j^T: lane = key, register r = query 8(r/4)+4hf+r%4
     f32x16 s, dp;
@@ -299,14 +321,15 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     }
 #pragma unroll
     for (int ds = 0; ds < L::NDS; ++ds) {
-      const bf16x8 a = as_bf16x8(ld16(sb_ + L::Q_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
+      const int off = n_lane ^ (ds << 5);
+      const bf16x8 a = as_bf16x8(ld16(sb_ + L::Q_OFF + off));
       s = mfma32(a, kf[ds], s);
-      const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_N + (l32 * L::NSTR + ds * 16 + 8 * hf) * 2));
+      const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_OFF + off));
       dp = mfma32(g, vf[ds], dp);
     }
     sched_reads_ahead<2 * L::NDS>();
-    const float* lsv = reinterpret_cast<const float*>(sb_ + L::L_F);
-    const float* dsv_ = reinterpret_cast<const float*>(sb_ + L::D_F);
+    const float* lsv = reinterpret_cast<const float*>(sb_ + L::L_OFF);
+    const float* dsv_ = reinterpret_cast<const float*>(sb_ + L::D_OFF);
     float p[16], dsv[16];
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -350,22 +373,32 @@ void bwd_kv_w4_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int db = 0; db < L::NDB; ++db) {
-        const bf16x8 g = as_bf16x8(ld16(sb_ + L::G_T + ((db * 32 + l32) * L::TSTR + 16 * t2 + 8 * hf) * 2));
-        dv[db] = mfma32(pb[t2], g, dv[db]);
-        const bf16x8 qq = as_bf16x8(ld16(sb_ + L::Q_T + ((db * 32 + l32) * L::TSTR + 16 * t2 + 8 * hf) * 2));
-        dk[db] = mfma32(sbf[t2], qq, dk[db]);
+        dv[db] = mfma32(pb[t2], tr_operand(sb_ + L::G_OFF, t2, db), dv[db]);
+        dk[db] = mfma32(sbf[t2], tr_operand(sb_ + L::Q_OFF, t2, db), dk[db]);
       }
-    sched_reads_ahead<4 * L::NDB>();
-    lstore(ST ^ 1);
-    wait_vmem_all();
-    __syncthreads();
+    sched_read_pairs_ahead<4 * L::NDB>();
+    // the next tile's copies (issued a step ago) have landed, for every wave;
+    // this step's reads are done before any wave copies over this stage
+    wait_vmem_le<L::COPIES>();
+    wait_lds_all();
+    barrier_keep_vmem();
   };
 
-  for (int s = 0; s < n; ++s) {
-    const int tn = tiles.next(tc + 1);
-    step(tc, tn, s & 1);
-    tc = tn;
+  int t0 = tiles.next(it0);                     // tiles of the next two steps
+  int t1 = tiles.next(t0 + 1);
+  copy_tile(t0, 0);
+  copy_tile(t1, 1);
+  wait_vmem_le<L::COPIES>();
+  barrier_keep_vmem();
+  for (int s = 0, st = 0; s < n; ++s) {
+    const int t2 = tiles.next(t1 + 1);
+    const int sf = st == 0 ? 2 : st - 1;        // (st + 2) % 3
+    step(t0, st, t2, sf);
+    t0 = t1;
+    t1 = t2;
+    st = st == 2 ? 0 : st + 1;
   }
+  wait_vmem_all();                              // no copy may land after the workgroup has left
 
   // dK_j = scale * dS^T Q, dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
   const unsigned gsz = grad_f32 ? 4u : 2u;
@@ -846,25 +879,6 @@ struct DqLayout {
   static constexpr int K_OFF = 0, V_OFF = KST;        // within a stage
 };
 
-// Chunk swizzle of row r of a K/V tile, for two kinds of reads.  Row reads (16
-// lanes = 16 consecutive rows, one 16-byte chunk each) need the swizzle to be a
-// permutation over any 16 rows (for 128-byte rows, two per 256-byte bank cycle:
-// over the row pairs).  Transposing reads (a half-wave = 4 consecutive rows x 4
-// chunks, 8 bytes per lane) need the four rows to spread a chunk group over all
-// bank groups: the row's position among the four moves chunk bits 2-3 (for
-// 128-byte rows, the odd row pair flips bit 2).  The swizzle changes chunk bits
-// >= 2 only through the row, so a 32-feature block's offset is a XOR with
-// (db << 6).
-template <int NC>
-__device__ __forceinline__ int dq_swz(int r) {
-  if constexpr (NC == 8) {
-    const int u = (r >> 1) & 7;
-    return u ^ ((u & 1) << 2);
-  } else {
-    return 4 * (r & 3) + ((r >> 2) & 3);
-  }
-}
-
 // Block-sparse dQ sweep: the workgroup's 256 queries span two 128-query mask
 // rows.  Both rows go into LDS bitmaps (bit c = key block c visible); the
 // workgroup visits the key tiles that either row can see, and a wave computes
@@ -962,7 +976,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     for (int i = 0; i < L::KDMA_W; ++i) {
       const int s = ((wave * L::KDMA_W + i) % L::KDMA) * 64 + lane;
       const int row = s / L::NC, cp = s % L::NC;
-      kvoff[i] = (unsigned)(row * D + (cp ^ dq_swz<L::NC>(row)) * 8) * 2u;
+      kvoff[i] = (unsigned)(row * D + (cp ^ row_swz<L::NC>(row)) * 8) * 2u;
     }
     const unsigned* const kvo = kvoff;   // (the host compiler drops a kernel whose lambdas index a captured array)
     auto kv_dma = [&](int k0, int st) {
@@ -976,7 +990,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
       }
     };
     // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
-    const int swz_l = dq_swz<L::NC>(lq);
+    const int swz_l = row_swz<L::NC>(lq);
     const int kbase_lane = lq * D * 2 + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
 
     // ---- K^T operand (A of dQ^T += K^T dS^T): lane l, row feature 32 db + l % 32,
@@ -990,7 +1004,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     for (int sec = 0; sec < 2; ++sec) {
       const int row = 8 * sec + 4 * (tg >> 1) + (ti >> 2);
       const int c = 2 * (tg & 1) + ((ti & 3) >> 1);
-      tb[sec] = row * L::RB + ((c ^ dq_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
+      tb[sec] = row * L::RB + ((c ^ row_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
     }
 
     f32x16 dq[L::NDB];

@@ -42,6 +42,32 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned nbytes) {
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, unsigned byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
+// The same buffer resource as four words, for inline assembly: base address
+// (48 bits), stride 0, size in bytes, and the flags word make_rsrc uses.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, unsigned nbytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, nbytes, 0x00020000u};
+}
+
+// buffer_load_dword{,x4} ... lds written out in assembly, HBM -> LDS: lane l's
+// 4 (16) bytes from byte offset voff of the resource land at LDS byte address
+// lds + 4 l (16 l); lds is wave-uniform and goes through M0.  The compiler does
+// not see these as LDS writes, so it adds no waits for them: the caller waits
+// with wait_vmem_le / wait_vmem_all before a barrier that hands the data on.
+// (M0 is reserved for the compiler, which sets it before each of its own uses;
+// no kernel that uses these also issues the builtin LDS copies.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_unseen(const u32x4& rsrc, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_unseen(const u32x4& rsrc, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
 
@@ -138,6 +164,20 @@ __device__ __forceinline__ void sched_reads_ahead() {
   for (int i = 0; i < M - A; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+
+// The same for operands that take two reads each (transposing 8-byte reads):
+// the first 2 A reads go ahead, then two reads per MFMA.
+template <int M, int A0 = 4>
+__device__ __forceinline__ void sched_read_pairs_ahead() {
+  constexpr int A = A0 < M ? A0 : M;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
+#pragma unroll
+  for (int i = 0; i < M - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
 }
