@@ -867,7 +867,12 @@ struct DqLayout {
   static constexpr int RB = D * 2;                     // bytes per K/V row
   static constexpr int KST = BC * RB;                  // K (or V) tile, swizzled rows, unpadded
   static constexpr int STAGE = 2 * KST;
-  static constexpr int BYTES = 2 * STAGE;
+  // d = 256 runs its sweep with the stage as a run-time index, over three stages
+  // filled two key blocks ahead by copies the compiler does not see (it cannot
+  // tell one array's stages apart and would wait for every copy in flight before
+  // each transposing read); d <= 128 unrolls two steps over two stage arrays.
+  static constexpr int NSTAGE = D == 256 ? 3 : 2;
+  static constexpr int BYTES = NSTAGE * STAGE;
   static constexpr int NKB = BC / 32;
   static constexpr int NDB = D / 32;
   static constexpr int NDS = D / 16;
@@ -899,7 +904,8 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   // need not wait for the DMA in flight into the other).
   __shared__ __attribute__((aligned(1024))) char stage0[L::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[L::STAGE];
-  auto stage_ptr = [&](int st) -> char* { return st == 0 ? stage0 : stage1; };
+  __shared__ __attribute__((aligned(1024))) char stage2[L::NSTAGE == 3 ? L::STAGE : 1024];
+  auto stage_ptr = [&](int st) -> char* { return st == 0 ? stage0 : st == 1 ? stage1 : stage2; };
 
   // Plain causal: workgroup p of a head runs query block nqb-1-p, then block p
   // (the long block first, as in the forward), so every workgroup sweeps about
@@ -966,7 +972,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 
     // ---- K (waves 0-3) and V (waves 4-7): HBM -> LDS, swizzled.  Lane l of DMA
     // instruction g moves chunk s = 64 (g % KDMA) + l of the tile: row s / NC,
-    // stored chunk s % NC, which holds source chunk (s % NC) ^ swizzle(row).  The
+    // stored chunk s % NC, which holds source chunk (s % NC) ^ row_swz(row).  The
     // lane offsets do not change between tiles; the tile's start goes into a
     // buffer resource over rows k0 .. Tk-1 (scalar work only), so rows past Tk --
     // and whole tiles past the end -- read as zeros.
@@ -981,12 +987,21 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     const unsigned* const kvo = kvoff;   // (the host compiler drops a kernel whose lambdas index a captured array)
     auto kv_dma = [&](int k0, int st) {
       const int rows = Tk - k0;
-      const rsrc_t r = make_rsrc(kv_src + kbase + (size_t)(k0 < Tk ? k0 : 0) * D, rows > 0 ? (unsigned)rows * D * 2u : 0u);
+      const unsigned nbytes = rows > 0 ? (unsigned)rows * D * 2u : 0u;
+      const uint16_t* const src = kv_src + kbase + (size_t)(k0 < Tk ? k0 : 0) * D;
+      if constexpr (L::NSTAGE == 3) {
+        const u32x4 r = raw_rsrc(src, nbytes);
+        const unsigned base = (unsigned)(size_t)stage_ptr(st) + wave * L::KDMA_W * 1024;
 #pragma unroll
-      for (int i = 0; i < L::KDMA_W; ++i) {
-        const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, kvo[i], 0, 0, 0);
+        for (int i = 0; i < L::KDMA_W; ++i) dma16_unseen(r, kvo[i], base + i * 1024);
+      } else {
+        const rsrc_t r = make_rsrc(src, nbytes);
+#pragma unroll
+        for (int i = 0; i < L::KDMA_W; ++i) {
+          const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, kvo[i], 0, 0, 0);
+        }
       }
     };
     // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
@@ -1060,15 +1075,24 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
     const int j0 = next_tile(jfirst);
     kv_dma(first_row(j0), 0);
-    wait_vmem_all();
-    __syncthreads();
+    int j1 = ntile;                                     // NSTAGE 3: the tile after j0, copied ahead too
+    if constexpr (L::NSTAGE == 3) {
+      j1 = next_tile(j0 + 1);
+      kv_dma(first_row(j1), 1);
+      wait_vmem_le<L::KDMA_W>();
+      barrier_keep_vmem();
+    } else {
+      wait_vmem_all();
+      __syncthreads();
+    }
 
-    // tile j in stage ST (the step's parity in the sweep); jn is the tile after it
-    auto step = [&](int j, int jn, int ST) {
+    // tile j in stage ST; tile jc is copied into stage SC (the next stage with two
+    // stages, two ahead with three)
+    auto step = [&](int j, int ST, int jc, int SC) {
       // the mask test comes before the loads of block jn: a branch between those
       // loads and the reads of stage ST would make the compiler wait for the loads
       const bool sees = wave_sees(j);
-      kv_dma(first_row(jn), ST ^ 1);
+      kv_dma(first_row(jc), SC);
       const int kt0 = j * BC;
       const bool in_band = BAND == 0 || (kt0 <= wb_hi && kt0 + BC - 1 >= wb_lo);
       if ((!CAUSAL || kt0 <= qw + 31) && sees && in_band) {   // some key of the block is visible to this wave
@@ -1151,8 +1175,17 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
             for (int db = 0; db < L::NDB; ++db) dq[db] = mfma32(ta[t][db], sf[t], dq[db]);
         }
       }
-      wait_vmem_all();
-      __syncthreads();
+      if constexpr (L::NSTAGE == 3) {
+        // this wave's copies of the next tile have landed (they complete in issue
+        // order; the ones just issued may still be in flight), and no wave reads
+        // this stage again before the copy two steps on overwrites it
+        wait_vmem_le<L::KDMA_W>();
+        wait_lds_all();
+        barrier_keep_vmem();
+      } else {
+        wait_vmem_all();
+        __syncthreads();
+      }
     };
 
     // The three loop forms compile differently; each is used where it needs no
@@ -1160,25 +1193,28 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     // constant; d = 256 runs one step per iteration with the stage offset
     // computed at run time.
     if constexpr (D == 256) {
-      for (int j = j0, st = 0; j < ntile; st ^= 1) {
-        const int jn = next_tile(j + 1);
-        step(j, jn, st);
-        j = jn;
+      for (int j = j0, st = 0; j < ntile;) {
+        const int j2 = next_tile(j1 + 1);
+        step(j, st, j2, st == 0 ? 2 : st - 1);
+        j = j1;
+        j1 = j2;
+        st = st == 2 ? 0 : st + 1;
       }
+      wait_vmem_all();   // the copies of tiles past the sweep, before this wave copies into the stages again
     } else if constexpr (MASKED) {
       for (int j = j0; j < ntile;) {
         int jn = next_tile(j + 1);
-        step(j, jn, 0);
+        step(j, 0, jn, 1);
         j = jn;
         if (j >= ntile) break;
         jn = next_tile(j + 1);
-        step(j, jn, 1);
+        step(j, 1, jn, 0);
         j = jn;
       }
     } else {
       for (int j = j0; j < ntile; j += 2) {
-        step(j, j + 1, 0);
-        if (j + 1 < ntile) step(j + 1, j + 2, 1);
+        step(j, 0, j + 1, 1);
+        if (j + 1 < ntile) step(j + 1, 1, j + 2, 0);
       }
     }
 
