@@ -481,49 +481,46 @@ __global__ __launch_bounds__(256) void row_terms_kernel(const uint16_t* __restri
 //     on MFMA (the accumulator starts at -D), P = exp2(S c log2e - lse log2e)
 //     and dS = P * (dP - D) ([ZtF] "The backward pass, derived", Observations
 //     1-3), handed on through LDS as MFMA fragments (P^T and dS^T, one key per
-//     lane).  lse and D of the next tile are fetched from HBM into registers
-//     while the current tile is processed.
+//     lane).
 //   * gradient waves 4-7 (wave 4+w serves score wave w's keys) keep dV_j and
 //     dK_j in float32 registers and trail the score waves by one query tile:
-//     dV_j += P^T dO_i and dK_j += dS^T Q_i; they also stage Q_i and dO_i two
-//     tiles ahead.
-// One barrier per phase orders everything: the row-major stages and the
-// fragment buffers alternate between two slots, the transposed Q/dO tiles
-// between three (the gradient waves read tile i-1's while writing tile i+1's);
-// the loops are unrolled so that every slot is a constant offset.  The barrier
-// is a bare s_barrier after the wave's own LDS writes have completed: a fence
-// would also wait for the prefetches (lse and D of the next tile, Q and dO two
-// tiles ahead) that are meant to stay in flight across it.
+//     dV_j += P^T dO_i and dK_j += dS^T Q_i.  They also issue the copies.
+// Q_i, dO_i, Ln_i and Dn_i (the negated row terms) go HBM -> LDS by
+// buffer_load ... lds, two tiles ahead, into a ring of four stages (the score
+// waves read tile i's while the gradient waves read tile i-1's, tile i+1's has
+// landed and tile i+2's is in flight); Q_i and dO_i rows are chunk-swizzled
+// (row_swz).  One row-major copy serves both roles: row reads for the score
+// waves' products over features, transposing 8-byte reads (one feature per
+// lane, queries in the k-slot order of the fragments) for the gradient waves'
+// products over queries.  The copies are issued in inline assembly, which the
+// compiler does not see, so it adds no wait for them before LDS reads of other
+// stages; the gradient waves wait for their own copies of the next tile before
+// the barrier that closes a phase.  One bare s_barrier per phase orders
+// everything, after the wave's own LDS writes (the fragments) have completed.
 // Rows past Tq and keys past Tk need no masking: their Q/dO or K/V rows read
 // as zeros, so they add nothing to the gradients that are stored.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvLayout {
-  // Row-major Q_i / dO_i tiles: 16-byte chunk c of query row r sits at
-  // (r % 4) NB + (8 c + r / 4) 16.  A staging store (rows 4 qa + i, chunk fg,
-  // lane = 8 fg + qa) then covers consecutive 16-byte slots, and the 16 lanes of
-  // a score-wave read (rows r0 .. r0 + 15, one chunk) fall in 16 distinct bank
-  // groups thanks to the 64-byte pad between the four row classes.  The read of
-  // k-step ds sits at the lane's base + 256 ds.  (With plain rows of D + 8 bf16
-  // the staging stores conflicted.)
-  static constexpr int NB = 16 * D + 64;        // bytes of one row class (r % 4)
-  static constexpr int TSTR = kBQ + 8;          // transposed tiles: D rows of 32 queries
-  static constexpr int N_BYTES = 4 * NB;
-  static constexpr int T_BYTES = D * TSTR * 2;
-  static constexpr int Q_N = 0;                              // one stage: Q_i and dO_i row-major
-  static constexpr int G_N = Q_N + N_BYTES;
-  static constexpr int STAGE = G_N + N_BYTES;
-  static constexpr int QT_OFF = 2 * STAGE;                   // Q_i^T, three slots
-  static constexpr int GT_OFF = QT_OFF + 3 * T_BYTES;        // dO_i^T, three slots
+  static constexpr int NC = D / 8;                           // 16-byte chunks per row
+  static constexpr int RB = D * 2;                           // bytes per row
+  static constexpr int TB = kBQ * RB;                        // one Q or dO tile
+  static constexpr int Q_OFF = 0;                            // byte offsets inside one stage
+  static constexpr int G_OFF = TB;
+  static constexpr int L_OFF = 2 * TB;                       // Ln: 64 floats (the second 32 unused)
+  static constexpr int D_OFF = L_OFF + 256;                  // Dn: likewise
+  static constexpr int X_OFF = D_OFF + 256;                  // gradient waves 6 and 7 copy row terms here, unused
+  static constexpr int STAGE = X_OFF + 512;
+  static constexpr int NSTAGE = 4;
+  static constexpr int F_OFF = NSTAGE * STAGE;               // fragments, two slots
   static constexpr int F_WAVE = 4 * 64 * 16;                 // P^T and dS^T fragments of one score wave
   static constexpr int F_BYTES = kWavesB * F_WAVE;
-  static constexpr int F_OFF = GT_OFF + 3 * T_BYTES;         // two slots
   static constexpr int BYTES = F_OFF + 2 * F_BYTES;
   static constexpr int NDS = D / 16;
   static constexpr int NDB = D / 32;
-  static constexpr int WPT = D / 64;                         // staging waves per tensor
-  static constexpr int SW0 = 8 - 2 * WPT;                    // first staging wave
-  static_assert(STAGE % 16 == 0 && T_BYTES % 16 == 0, "16-byte aligned regions");
+  static constexpr int DMA_W = TB / 1024 / 2;                // 1 KiB copies per gradient wave (two per tensor)
+  static constexpr int COPIES = DMA_W + 1;                   // copies a gradient wave issues per tile
+  static_assert(STAGE % 1024 == 0 && COPIES <= 15, "stage alignment; vmcnt field");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -535,7 +532,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
     const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr,
     const int* __restrict__ cu, int nd, int bcausal) {
   using L = KvLayout<D>;
-  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   // Plain causal at d = 128: workgroup p of a head runs key block p, then key
   // block nkb-1-p, so every workgroup sweeps about the same number of query
@@ -555,6 +552,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
   const int l32 = lane & 31, hf = lane >> 5;
   const int wq = wave & 3;                      // key slice (score wave w and gradient wave 4+w)
   const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
+  auto stage_ptr = [&](int st) { return smem + st * L::STAGE; };
   for (int pass = 0; pass < npass; ++pass) {
     const int kblk = pass == 0 ? pidx : nkb - 1 - pidx;
     if (pass > 0) {
@@ -593,8 +591,6 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
       // ============================ score waves ============================
       const rsrc_t rk = make_rsrc(K + kbase, (unsigned)Tk * D * 2u);
       const rsrc_t rv = make_rsrc(V + kbase, (unsigned)Tk * D * 2u);
-      const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
-      const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
       bf16x8 kf[L::NDS], vf[L::NDS];
 #pragma unroll
       for (int ds = 0; ds < L::NDS; ++ds) {
@@ -602,52 +598,42 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
         kf[ds] = as_bf16x8(bload16(rk, off));
         vf[ds] = as_bf16x8(bload16(rv, off));
       }
-      // -lse log2e and -D of the tile's queries in the accumulator order:
-      // register r <-> query 8(r/4) + 4hf + r%4 (all lanes of a half alike)
-      auto terms_load = [&](int t, f32x16& lt, f32x16& dt) {
-        const int r0 = tile_row(t);
+      // this lane's row read for k-step ds: chunk (2 ds + hf) ^ swz of query row l32
+      const int swz_l = row_swz<L::NC>(l32);
+      const int n_lane = l32 * L::RB + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
+      int tc = next_tile(it0);                      // the tile of the next score step
+      barrier_keep_vmem();
+
+      // tile t in stage st, fragments into slot fs
+      for (int s = 0; s < n; ++s) {
+        const int t = tc;
+        tc = next_tile(tc + 1);
+        const int r0 = t * kBQ;
+        const char* sb_ = stage_ptr(s & (L::NSTAGE - 1));
+        // -lse log2e and -D of the tile's queries in the accumulator order:
+        // register r <-> query 8(r/4) + 4hf + r%4 (all lanes of a half alike)
+        f32x16 lt, dp;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const unsigned off = (unsigned)(r0 + 8 * g4 + 4 * hf) * 4u;
-          const f32x4 a = __builtin_bit_cast(f32x4, bload16(rl, off));
-          const f32x4 b = __builtin_bit_cast(f32x4, bload16(rd, off));
+          const f32x4 a = *reinterpret_cast<const f32x4*>(sb_ + L::L_OFF + (8 * g4 + 4 * hf) * 4);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(sb_ + L::D_OFF + (8 * g4 + 4 * hf) * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             lt[4 * g4 + e] = a[e];
-            dt[4 * g4 + e] = b[e];
+            dp[4 * g4 + e] = b[e];
           }
         }
-      };
-      // this lane's row-major operand reads: query row l32, chunk 2 ds + hf (layout in KvLayout)
-      const int n_lane = (l32 & 3) * L::NB + (8 * hf + (l32 >> 2)) * 16;
-      f32x16 lt0, dt0, lt1, dt1;
-      int tc = next_tile(it0);                      // the tile of the next score step
-      terms_load(tc, lt0, dt0);
-      barrier_keep_vmem();
-
-      // tile t in stage ST (the step's parity in the sweep); tn is the tile after it
-      auto score_step = [&](int t, int tn, auto stage, const f32x16& lt, const f32x16& dt, f32x16& lt_n,
-                            f32x16& dt_n) {
-        constexpr int ST = decltype(stage)::value;
-        terms_load(tn, lt_n, dt_n);
-        const int r0 = t * kBQ;
-        const char* sb_ = smem + ST * L::STAGE;
         // S = Q_i K_j^T and dP - D = dO_i V_j^T - D_i: lane = key, register r = query 8(r/4)+4hf+r%4
-        f32x16 sacc, dp = dt;
+        f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-        bf16x8 qa[L::NDS], ga[L::NDS];
 #pragma unroll
         for (int ds = 0; ds < L::NDS; ++ds) {
-          qa[ds] = as_bf16x8(ld16(sb_ + L::Q_N + n_lane + ds * 256));
-          ga[ds] = as_bf16x8(ld16(sb_ + L::G_N + n_lane + ds * 256));
+          const int off = n_lane ^ (ds << 5);
+          sacc = mfma32(as_bf16x8(ld16(sb_ + L::Q_OFF + off)), kf[ds], sacc);
+          dp = mfma32(as_bf16x8(ld16(sb_ + L::G_OFF + off)), vf[ds], dp);
         }
-#pragma unroll
-        for (int ds = 0; ds < L::NDS; ++ds) {
-          sacc = mfma32(qa[ds], kf[ds], sacc);
-          dp = mfma32(ga[ds], vf[ds], dp);
-        }
-        sched_reads_ahead<2 * L::NDS>();
+        sched_reads_ahead<2 * L::NDS, 2 * L::NDS + 8, 6>();
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sacc[r], cl2e, lt[r]));
@@ -664,73 +650,81 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
           }
         }
         // fragments for the gradient wave: [P^T t=0, P^T t=1, dS^T t=0, dS^T t=1], 1 KiB each
-        char* fb = smem + L::F_OFF + ST * L::F_BYTES + wq * L::F_WAVE + lane * 16;
+        char* fb = smem + L::F_OFF + (s & 1) * L::F_BYTES + wq * L::F_WAVE + lane * 16;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t2 = 0; t2 < 2; ++t2) {
           u32x4 a, b;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 8 * t + 2 * e;
+            const int r = 8 * t2 + 2 * e;
             a[e] = pack_bf16(p[r], p[r + 1]);
             b[e] = pack_bf16(p[r] * dp[r], p[r + 1] * dp[r + 1]);
           }
-          st16(fb + t * 1024, a);
-          st16(fb + (2 + t) * 1024, b);
+          st16(fb + t2 * 1024, a);
+          st16(fb + (2 + t2) * 1024, b);
         }
-        // the fragments are complete; lse and D of the next tile stay in flight
+        // the fragments are complete, and so are this step's reads of the stage
         wait_lds_all();
         barrier_keep_vmem();
-      };
-      for (int s = 0; s < n; s += 2) {
-        int tn = next_tile(tc + 1);
-        score_step(tc, tn, std::integral_constant<int, 0>{}, lt0, dt0, lt1, dt1);
-        tc = tn;
-        if (s + 1 < n) {
-          tn = next_tile(tc + 1);
-          score_step(tc, tn, std::integral_constant<int, 1>{}, lt1, dt1, lt0, dt0);
-          tc = tn;
-        }
       }
     } else {
       // =========================== gradient waves ==========================
-      const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
-      const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
-
-      // Staging: WPT waves per tensor (Q, then dO); lane sidx = 8 fg + qa holds 4
-      // consecutive query rows (quad qa) x 8 features (group fg).  A tile index
-      // past the sweep maps to row Tq, whose loads return zeros.
-      const bool stager = wave >= L::SW0;
-      const bool is_g = wave >= L::SW0 + L::WPT;
-      const int sidx = ((wave - L::SW0) % L::WPT) * 64 + lane;
-      const int qa = sidx & 7, fg = sidx >> 3;
-      const rsrc_t rsrc = is_g ? rg : rq;
-      // transposed position of the quad: the middle quads of each 16 queries are
-      // swapped, matching the query order of a fragment's MFMA k-slots
-      const int tpos = 16 * (qa >> 2) + 4 * (((qa & 1) << 1) | ((qa >> 1) & 1));
-      const int n_off = (is_g ? L::G_N : L::Q_N) + sidx * 16;     // row 4 qa + i, chunk fg: i NB + 16 sidx
-      const int t_off = (is_g ? L::GT_OFF : L::QT_OFF) + ((fg * 8) * L::TSTR + tpos) * 2;
-      u32x4 stg[4];
-      auto gload = [&](int t) {
-        if (stager) {
-          const int r0 = tile_row(t);
+      // Copies of one tile into a stage.  Waves 4-5 move Q_i, waves 6-7 dO_i:
+      // lane l of copy g (0 .. 2 DMA_W - 1 over the tensor's two waves) moves
+      // chunk s = 64 g + l of the tile, row s / NC, stored at chunk s % NC,
+      // which holds source chunk (s % NC) ^ row_swz(row).  Wave 4 also copies
+      // Ln_i and wave 5 Dn_i (64 floats from the tile's first row); waves 6 and
+      // 7 make the same copies into an unused slot, so that every gradient wave
+      // issues COPIES per tile.  The lane offsets do not change between tiles;
+      // the tile's first row goes into a buffer resource over rows r0 .. Tq-1,
+      // so rows past Tq -- and whole tiles past the sweep, which start at row Tq
+      // -- read as zeros.
+      const int gw = wave - 4;
+      const bool is_g = gw >= 2;
+      const uint16_t* const src = is_g ? dO : Q;
+      unsigned coff[L::DMA_W];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) stg[i] = bload16(rsrc, ((unsigned)(r0 + 4 * qa + i) * D + fg * 8) * 2u);
-        }
+      for (int i = 0; i < L::DMA_W; ++i) {
+        const int s = ((gw & 1) * L::DMA_W + i) * 64 + lane;
+        const int row = s / L::NC, cp = s % L::NC;
+        coff[i] = (unsigned)(row * D + (cp ^ row_swz<L::NC>(row)) * 8) * 2u;
+      }
+      const unsigned* const co = coff;   // (the host compiler drops a kernel whose lambdas index a captured array)
+      const float* const terms = ((gw & 1) ? Dn : Ln) + (size_t)bh * Tq;
+      const unsigned lds0 = (unsigned)(size_t)smem;
+      const unsigned t_dst = (gw & 1) ? L::D_OFF : L::L_OFF;
+      const unsigned x_dst = is_g ? L::X_OFF + 256 * (gw & 1) : t_dst;
+      const unsigned c_dst = (is_g ? L::G_OFF : L::Q_OFF) + (gw & 1) * L::DMA_W * 1024;
+      auto copy_tile = [&](int t, int st) {
+        const int r0 = tile_row(t);
+        const int rows = Tq - r0;
+        const unsigned base = lds0 + (unsigned)st * L::STAGE;
+        const u32x4 r = raw_rsrc(src + qbase + (size_t)(r0 < Tq ? r0 : 0) * D, rows > 0 ? (unsigned)rows * D * 2u : 0u);
+#pragma unroll
+        for (int i = 0; i < L::DMA_W; ++i) dma16_unseen(r, co[i], base + c_dst + i * 1024);
+        const u32x4 rt = raw_rsrc(terms + (r0 < Tq ? r0 : 0), rows > 0 ? (unsigned)rows * 4u : 0u);
+        dma4_unseen(rt, (unsigned)lane * 4u, base + x_dst);
       };
-      auto lstore = [&](int slot2, int slot3) {     // slots s % 2 and s % 3 of the tile staged
-        if (stager) {
-          char* N = smem + slot2 * L::STAGE + n_off;
-          char* T = smem + slot3 * L::T_BYTES + t_off;
+
+      // transposing reads (B operands of the products over queries): lane l gets
+      // feature 32 db + l % 32, queries 16 t + 4 hf + 0..3 and 16 t + 8 + 4 hf +
+      // 0..3 of the tile -- the k-slot order of the fragments.  Each half comes
+      // from one read in which lane 16 g + 4 e + j addresses query row
+      // 4 (g / 2) + e (+ 8 for the second half) and features 16 (g % 2) + 4 j ..
+      // +3; tb[sec] is that offset for t = db = 0.
+      const int tg = lane >> 4, ti = lane & 15;
+      int tb[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) st16(N + i * L::NB, stg[i]);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const u32x2 ev = {lo_lo(stg[0][w], stg[1][w]), lo_lo(stg[2][w], stg[3][w])};
-            const u32x2 od = {hi_hi(stg[0][w], stg[1][w]), hi_hi(stg[2][w], stg[3][w])};
-            st8(T + (2 * w) * L::TSTR * 2, ev);
-            st8(T + (2 * w + 1) * L::TSTR * 2, od);
-          }
-        }
+      for (int sec = 0; sec < 2; ++sec) {
+        const int row = 8 * sec + 4 * (tg >> 1) + (ti >> 2);
+        const int c = 2 * (tg & 1) + ((ti & 3) >> 1);
+        tb[sec] = row * L::RB + ((c ^ row_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
+      }
+      auto tr_operand = [&](const char* tile, int t, int db) {
+        const char* base = tile + t * 16 * L::RB;
+        const u32x2 lo = ld8_tr(base + (tb[0] ^ (db << 6)));
+        const u32x2 hi = ld8_tr(base + (tb[1] ^ (db << 6)));
+        return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       };
 
       f32x16 dk[L::NDB], dv[L::NDB];
@@ -742,73 +736,54 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
           dv[db][r] = 0.f;
         }
       const int f_lane = L::F_OFF + wq * L::F_WAVE + lane * 16;
-      const int t_lane = (l32 * L::TSTR + 8 * hf) * 2;
 
-      // dV_j += P^T dO_i and dK_j += dS^T Q_i for the tile in slots (slot2, slot3):
-      // lane = feature column, register = key row
-      auto grad_step = [&](int slot2, int slot3) {
-        const char* fb = smem + slot2 * L::F_BYTES + f_lane;
-        const char* gt = smem + L::GT_OFF + slot3 * L::T_BYTES + t_lane;
-        const char* qt = smem + L::QT_OFF + slot3 * L::T_BYTES + t_lane;
-        bf16x8 pb[2], sbf[2], ga[2][L::NDB], qa[2][L::NDB];
+      // dV_j += P^T dO_i and dK_j += dS^T Q_i for the tile in stage st with its
+      // fragments in slot fs: lane = feature column, register = key row
+      auto grad_step = [&](int st, int fs) {
+        const char* fb = smem + fs * L::F_BYTES + f_lane;
+        const char* sb_ = stage_ptr(st);
+        bf16x8 pb[2], sbf[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           pb[t] = as_bf16x8(ld16(fb + t * 1024));
           sbf[t] = as_bf16x8(ld16(fb + (2 + t) * 1024));
-#pragma unroll
-          for (int db = 0; db < L::NDB; ++db) {
-            const int toff = (db * 32 * L::TSTR + 16 * t) * 2;
-            ga[t][db] = as_bf16x8(ld16(gt + toff));
-            qa[t][db] = as_bf16x8(ld16(qt + toff));
-          }
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < L::NDB; ++db) {
-            dv[db] = mfma32(pb[t], ga[t][db], dv[db]);
-            dk[db] = mfma32(sbf[t], qa[t][db], dk[db]);
+            dv[db] = mfma32(pb[t], tr_operand(sb_ + L::G_OFF, t, db), dv[db]);
+            dk[db] = mfma32(sbf[t], tr_operand(sb_ + L::Q_OFF, t, db), dk[db]);
           }
-        sched_reads_ahead<4 * L::NDB, 4 * L::NDB + 4>();
+        sched_read_pairs_ahead<4 * L::NDB, 4, 4>();
       };
 
       int tgr = next_tile(it0);                        // the tile of the next gradient step
-      int tg = tgr;                                    // the tile of the next fetch
-      if (n > 0) {
-        gload(tg);
-        lstore(0, 0);
-        tg = next_tile(tg + 1);
-        if (n > 1) {
-          gload(tg);
-          tg = next_tile(tg + 1);
-        }
-      }
-      wait_lds_all();
+      int t1 = next_tile(tgr + 1);                     // the tiles copied next
+      int t2 = next_tile(t1 + 1);
+      copy_tile(tgr, 0);
+      copy_tile(t1, 1);
+      wait_vmem_le<L::COPIES>();
       barrier_keep_vmem();
-      // phase p: gradients of sweep step p-1, stage step p+1, fetch step p+2.
-      // m2 = p % 2 and m3 = p % 3 (wave-uniform counters) pick the slots.
-      int m2 = 0, m3 = 0;
+      // phase p: the score waves' step p; here the gradients of step p-1 and the
+      // copy of step p+2's tile, into stage (p+2) % 4 (last read in phase p-1)
       for (int p = 0; p < n; ++p) {
-        const int up3 = m3 == 2 ? 0 : m3 + 1;          // (p + 1) % 3
-        const int dn3 = m3 == 0 ? 2 : m3 - 1;          // (p - 1) % 3
+        copy_tile(t2, (p + 2) & (L::NSTAGE - 1));
+        t2 = next_tile(t2 + 1);
         if (p >= 1) {
           // causal: a query tile wholly before this wave's keys has all-zero fragments
-          if (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0) grad_step(m2 ^ 1, dn3);
+          if (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0) grad_step((p - 1) & (L::NSTAGE - 1), (p - 1) & 1);
           tgr = next_tile(tgr + 1);
         }
-        if (p + 1 < n) lstore(m2 ^ 1, up3);
-        if (p + 2 < n) {
-          gload(tg);
-          tg = next_tile(tg + 1);
-        }
-        // the staged tile is in LDS; the fetch of tile p+2 stays in flight
+        // this wave's copies of step p+1's tile have landed (they complete in
+        // issue order; step p+2's may still be in flight), and its reads are done
+        wait_vmem_le<L::COPIES>();
         wait_lds_all();
         barrier_keep_vmem();
-        m2 ^= 1;
-        m3 = up3;
       }
-      // the last tile's gradients: its slots are ((n-1) % 2, (n-1) % 3)
-      if (n > 0 && (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0)) grad_step(m2 ^ 1, m3 == 0 ? 2 : m3 - 1);
+      // the last tile's gradients (stage and fragment slot of step n-1)
+      if (n > 0 && (!CAUSAL || tgr * kBQ + kBQ - 1 >= kw0)) grad_step((n - 1) & (L::NSTAGE - 1), (n - 1) & 1);
+      wait_vmem_all();                                 // no copy may land after the block is done
 
       // dK_j = scale * dS^T Q and dV_j: lane = feature, register r = key 8(r/4)+4hf+r%4
       const unsigned gsz = grad_f32 ? 4u : 2u;

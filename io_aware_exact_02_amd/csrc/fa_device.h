@@ -168,12 +168,13 @@ __device__ __forceinline__ void sched_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
 }
 
-// The same for operands that take two reads each (transposing 8-byte reads):
-// the first 2 A reads go ahead, then two reads per MFMA.
-template <int M, int A0 = 4>
+// The same for operands that take two reads each (transposing 8-byte reads),
+// after E reads of other operands: the first E + 2 A reads go ahead, then two
+// reads per MFMA.
+template <int M, int A0 = 4, int E = 0>
 __device__ __forceinline__ void sched_read_pairs_ahead() {
   constexpr int A = A0 < M ? A0 : M;
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * A, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, E + 2 * A, 0);
 #pragma unroll
   for (int i = 0; i < M - A; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
