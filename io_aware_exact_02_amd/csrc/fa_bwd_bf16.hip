@@ -1213,6 +1213,300 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   }
 }
 
+// ---------------------------------------------------------------------------
+// Query-block sweep for d = 256 in two roles (bwd_dq_split_kernel).
+//
+// With one wave per query slice, the Q and dO fragments (128 registers per
+// lane), the dQ^T accumulator (128) and the S/dP accumulators oversubscribe a
+// wave's registers, and the compiler shuttles the accumulator between AGPRs and
+// VGPRs around every dQ product.  Here a workgroup of eight waves covers 128
+// queries, two waves per 32-query slice and per SIMD:
+//   * score wave w (0-3) keeps slice w's Q and dO fragments, lse and D, forms
+//     S^T = K_j Q^T and dP^T - D, then P^T and dS^T ([ZtF] "The backward pass,
+//     derived"), and hands dS^T on through LDS as two MFMA fragments;
+//   * gradient wave 4+w keeps slice w's dQ^T accumulator and trails its score
+//     wave by one key block: dQ^T += K_j^T dS^T, K_j^T by transposing reads from
+//     the same K tile.  The gradient waves also issue the copies.
+// K_j and V_j go HBM -> LDS by buffer_load ... lds (inline assembly, unseen by
+// the compiler) two blocks ahead into a ring of four stages; one bare barrier
+// per phase.  Each slice's arithmetic, and the order of its dQ sums, are those
+// of bwd_dq_kernel, so the results are the same bits.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqsLayout {
+  static constexpr int BR = 128;                       // query rows per workgroup (4 slices)
+  static constexpr int BC = 32;                        // keys per block
+  static constexpr int NC = D / 8;
+  static constexpr int RB = D * 2;
+  static constexpr int KST = BC * RB;                  // K (or V) tile, swizzled rows
+  static constexpr int STAGE = 2 * KST;
+  static constexpr int NSTAGE = 4;
+  static constexpr int F_OFF = NSTAGE * STAGE;         // dS^T fragments: 2 KiB per score wave, two slots
+  static constexpr int F_SLOT = 4 * 2048;
+  static constexpr int BYTES = F_OFF + 2 * F_SLOT;
+  static constexpr int NDS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int COPIES = STAGE / 1024 / 4;      // 1 KiB copies per gradient wave and block
+  static constexpr int K_OFF = 0, V_OFF = KST;
+  static_assert(NC >= 16 && STAGE % 1024 == 0 && COPIES <= 15, "layout");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+  static_assert(BR == kMaskBlock, "one mask row per workgroup");
+};
+
+template <int D, bool CAUSAL, bool MASKED, int BAND>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Ln, const float* __restrict__ Dn,
+    void* __restrict__ dQ, int Tq, int Tk, float scale, float cl2e, int nqb, int grad_f32,
+    const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk, int wl, int wr,
+    const int* __restrict__ cu, int nd, int bcausal) {
+  using L = DqsLayout<D>;
+  constexpr int BC = L::BC;
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+  auto stage_ptr = [&](int st) { return smem + st * L::STAGE; };
+
+  constexpr bool PAIRED = CAUSAL && !MASKED && BAND == 0;
+  const int nblk = gridDim.x, wid = blockIdx.x;
+  const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
+  const int npb = PAIRED ? (nqb + 1) / 2 : nqb;     // workgroups per head
+  const int bh = lin / npb;
+  const int pidx = lin % npb;
+  const int npass = (PAIRED && 2 * pidx + 1 < nqb) ? 2 : 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const int ws = wave & 3;                             // query slice (score wave ws, gradient wave 4+ws)
+  const size_t qbase = (size_t)bh * Tq * D, kbase = (size_t)bh * Tk * D;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass > 0) {
+      // the previous block's last reads are done before its stages are reused
+      wait_lds_all();
+      barrier_keep_vmem();
+    }
+    const int qb = !CAUSAL ? pidx : (npass == 2 && pass == 1) ? pidx : nqb - 1 - pidx;
+    const int q0 = qb * L::BR;
+    const int qw = q0 + ws * 32;
+    const int myq = qw + lq;
+
+    int ntile = (Tk + BC - 1) / BC;
+    if (CAUSAL) ntile = min(ntile, (min(q0 + L::BR, Tq) - 1) / BC + 1);
+    int jfirst = 0;
+    int klo = 0, khi = 0, w_lo = 0, w_hi = 0, wb_lo = 0, wb_hi = 0;
+    if constexpr (BAND != 0) {
+      const Band<BAND> band{wl, wr, cu, nd, bcausal};
+      band.keys(myq, klo, khi);
+      w_lo = band.lo(qw + 31);
+      w_hi = band.hi(qw);
+      wb_lo = band.lo(qw);
+      wb_hi = band.hi(qw + 31);
+      const int b_hi = band.hi(min(q0 + L::BR, Tq) - 1);
+      ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
+      jfirst = max(0, band.lo(q0)) / BC;
+    }
+    // visible key blocks: bit c of word w of the block's mask row = key block 64w + c kept
+    const int nvw = (nmk + 63) >> 6;
+    const uint8_t* mrow = MASKED ? bmask + (long long)(bh % H) * mask_hstride + (long long)(q0 / kMaskBlock) * nmk
+                                 : nullptr;
+    int cw = -1;
+    unsigned long long ca = 0;
+    auto word = [&](int w) {
+      if (w != cw) {
+        cw = w;
+        ca = mask_word(mrow, 1, nmk, w, lane);
+      }
+      return ca;
+    };
+    auto next_tile = [&](int j) {                     // first visible block >= j, ntile if none
+      if constexpr (MASKED) {
+        if (j >= ntile) return ntile;
+        const int c = j * BC / kMaskBlock;
+        int w = c >> 6;
+        unsigned long long bits = word(w) & (~0ull << (c & 63));
+        while (bits == 0) {
+          if (++w >= nvw) return ntile;
+          bits = word(w);
+        }
+        const int c2 = w * 64 + (int)__builtin_ctzll(bits);
+        return c2 == c ? j : min(ntile, c2 * (kMaskBlock / BC));
+      } else {
+        return j;
+      }
+    };
+    // the tile's work for this slice: some key of the block visible to some row
+    auto visible = [&](int j) {
+      const int kt0 = j * BC;
+      const bool in_band = BAND == 0 || (kt0 <= wb_hi && kt0 + BC - 1 >= wb_lo);
+      return (!CAUSAL || kt0 <= qw + 31) && in_band;
+    };
+    const int j0 = next_tile(jfirst);
+
+    if (wave < 4) {
+      // ============================ score waves ============================
+      const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+      const rsrc_t rg = make_rsrc(dO + qbase, (unsigned)Tq * D * 2u);
+      const rsrc_t rl = make_rsrc(Ln + (size_t)bh * Tq, (unsigned)Tq * 4u);
+      const rsrc_t rd = make_rsrc(Dn + (size_t)bh * Tq, (unsigned)Tq * 4u);
+      bf16x8 qf[L::NDS], gf[L::NDS];
+#pragma unroll
+      for (int ds = 0; ds < L::NDS; ++ds) {
+        const unsigned off = ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u;
+        qf[ds] = as_bf16x8(bload16(rq, off));
+        gf[ds] = as_bf16x8(bload16(rg, off));
+      }
+      const float lnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, myq * 4, 0, 0));
+      const float dnq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, myq * 4, 0, 0));
+      // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
+      const int swz_l = row_swz<L::NC>(lq);
+      const int kbase_lane = lq * D * 2 + (((swz_l >> 1) << 5) | ((hf ^ (swz_l & 1)) << 4));
+      barrier_keep_vmem();
+      int p = 0;
+      for (int j = j0; j < ntile; ++p) {
+        const int jn = next_tile(j + 1);
+        if (visible(j)) {
+          const int kt0 = j * BC;
+          const bool edge = (CAUSAL && kt0 + BC - 1 > qw) || (kt0 + BC > Tk) ||
+                            (BAND != 0 && !(kt0 >= w_lo && kt0 + BC - 1 <= w_hi));
+          const char* sb_ = stage_ptr(p & (L::NSTAGE - 1));
+          // S^T and dP^T - D for the block's 32 keys: register r = key kt0 + 8(r/4)+4hf+r%4, lane = query
+          f32x16 s, dp;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[r] = 0.f;
+            dp[r] = dnq;
+          }
+#pragma unroll
+          for (int ds = 0; ds < L::NDS; ++ds) {
+            const int off = kbase_lane ^ (ds << 5);
+            s = mfma32(as_bf16x8(ld16(sb_ + L::K_OFF + off)), qf[ds], s);
+            dp = mfma32(as_bf16x8(ld16(sb_ + L::V_OFF + off)), gf[ds], dp);
+          }
+          sched_reads_ahead<2 * L::NDS, 2 * L::NDS, 10>();
+          float pr[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(__builtin_fmaf(s[r], cl2e, lnq));
+          if (edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kt0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (key >= Tk || (CAUSAL && key > myq) || (BAND != 0 && (key < klo || key > khi))) pr[r] = 0.f;
+            }
+          }
+          char* fb = smem + L::F_OFF + (p & 1) * L::F_SLOT + ws * 2048 + lane * 16;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * t + 2 * e;
+              w[e] = pack_bf16(pr[r] * dp[r], pr[r + 1] * dp[r + 1]);
+            }
+            st16(fb + t * 1024, w);
+          }
+        }
+        // the fragments are complete, and so are this step's reads of the stage
+        wait_lds_all();
+        barrier_keep_vmem();
+        j = jn;
+      }
+    } else {
+      // =========================== gradient waves ==========================
+      // Copies: waves 4-5 move K_j, waves 6-7 V_j; lane l of copy g (0 .. 2 COPIES
+      // - 1 over the tensor's two waves) moves chunk s = 64 g + l of the tile: row
+      // s / NC, stored at chunk s % NC, which holds source chunk (s % NC) ^
+      // row_swz(row).  A block index past the sweep starts at row Tk: zeros.
+      const int gw = wave - 4;
+      const uint16_t* const src = gw >= 2 ? V : K;
+      unsigned coff[L::COPIES];
+#pragma unroll
+      for (int i = 0; i < L::COPIES; ++i) {
+        const int sidx = ((gw & 1) * L::COPIES + i) * 64 + lane;
+        const int row = sidx / L::NC, cp = sidx % L::NC;
+        coff[i] = (unsigned)(row * D + (cp ^ row_swz<L::NC>(row)) * 8) * 2u;
+      }
+      const unsigned* const co = coff;   // (the host compiler drops a kernel whose lambdas index a captured array)
+      const unsigned lds0 = (unsigned)(size_t)smem;
+      const unsigned c_dst = (gw >= 2 ? L::V_OFF : L::K_OFF) + (gw & 1) * L::COPIES * 1024;
+      auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
+      auto copy_tile = [&](int j, int st) {
+        const int k0 = first_row(j);
+        const int rows = Tk - k0;
+        const u32x4 r = raw_rsrc(src + kbase + (size_t)(k0 < Tk ? k0 : 0) * D, rows > 0 ? (unsigned)rows * D * 2u : 0u);
+        const unsigned base = lds0 + (unsigned)st * L::STAGE + c_dst;
+#pragma unroll
+        for (int i = 0; i < L::COPIES; ++i) dma16_unseen(r, co[i], base + i * 1024);
+      };
+      // K^T operand (A of dQ^T += K^T dS^T): lane l, row feature 32 db + l % 32,
+      // elements = keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3, as in bwd_dq_kernel
+      const int tg = lane >> 4, ti = lane & 15;
+      int tb[2];
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int row = 8 * sec + 4 * (tg >> 1) + (ti >> 2);
+        const int c = 2 * (tg & 1) + ((ti & 3) >> 1);
+        tb[sec] = row * L::RB + ((c ^ row_swz<L::NC>(row)) << 4) + 8 * (ti & 1);
+      }
+      f32x16 dq[L::NDB];
+#pragma unroll
+      for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+      auto grad_step = [&](int st, int fs) {
+        const char* fb = smem + L::F_OFF + fs * L::F_SLOT + ws * 2048 + lane * 16;
+        const bf16x8 sf0 = as_bf16x8(ld16(fb)), sf1 = as_bf16x8(ld16(fb + 1024));
+        const char* ks = stage_ptr(st) + L::K_OFF;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) {
+            const u32x2 lo = ld8_tr(ks + 16 * t * L::RB + (tb[0] ^ (db << 6)));
+            const u32x2 hi = ld8_tr(ks + 16 * t * L::RB + (tb[1] ^ (db << 6)));
+            dq[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), t ? sf1 : sf0, dq[db]);
+          }
+        sched_read_pairs_ahead<2 * L::NDB, 4, 2>();
+      };
+      int jc1 = next_tile(j0 + 1);
+      int jc2 = next_tile(jc1 + 1);
+      copy_tile(j0, 0);
+      copy_tile(jc1, 1);
+      wait_vmem_le<L::COPIES>();
+      barrier_keep_vmem();
+      int p = 0, jprev = -1;
+      for (int j = j0; j < ntile; ++p) {
+        copy_tile(jc2, (p + 2) & (L::NSTAGE - 1));
+        jc2 = next_tile(jc2 + 1);
+        if (jprev >= 0 && visible(jprev)) grad_step((p - 1) & (L::NSTAGE - 1), (p - 1) & 1);
+        jprev = j;
+        j = next_tile(j + 1);
+        // this wave's copies of the next block have landed (they complete in issue
+        // order), and its reads of the stages are done
+        wait_vmem_le<L::COPIES>();
+        wait_lds_all();
+        barrier_keep_vmem();
+      }
+      if (jprev >= 0 && visible(jprev)) grad_step((p - 1) & (L::NSTAGE - 1), (p - 1) & 1);
+      wait_vmem_all();                                 // no copy may land after the block is done
+
+      if (myq >= Tq) continue;
+      // dQ: lane = query, register 4g+e of block db = feature db*32 + 8g + 4hf + e
+#pragma unroll
+      for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * hf;
+          const size_t off = qbase + (size_t)myq * D + d0;
+          const float v0 = scale * dq[db][4 * g], v1 = scale * dq[db][4 * g + 1];
+          const float v2 = scale * dq[db][4 * g + 2], v3 = scale * dq[db][4 * g + 3];
+          if (grad_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(dQ) + off) = (f32x4){v0, v1, v2, v3};
+          } else {
+            const u32x2 w = {pack_bf16(v0, v1), pack_bf16(v2, v3)};
+            st8(static_cast<uint16_t*>(dQ) + off, w);
+          }
+        }
+    }
+  }
+}
+
 template <int D>
 int bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* lse, void* dQ,
         void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int o_f32, int grad_f32,
@@ -1286,14 +1580,32 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
       hipLaunchKernelGGL(kernel, dim3((unsigned)ndq), dim3(LQ::THREADS), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq,
                          Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
     };
-    if (band == 1) dqk(bwd_dq_kernel<D, false, false, 1>);
-    else if (band == 2) dqk(bwd_dq_kernel<D, false, false, 2>);
-    else if (bmask) {
-      if (causal) dqk(bwd_dq_kernel<D, true, true, 0>);
-      else dqk(bwd_dq_kernel<D, false, true, 0>);
+    // d = 256: the two-role kernel, eight waves per 128 queries (same grid)
+    auto dqs = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)ndq), dim3(512), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq, Tk, scale,
+                         cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
+    };
+    if constexpr (D == 256) {
+      static_assert(DqsLayout<D>::BR == LQ::BR, "same query blocks");
+      if (band == 1) dqs(bwd_dq_split_kernel<D, false, false, 1>);
+      else if (band == 2) dqs(bwd_dq_split_kernel<D, false, false, 2>);
+      else if (bmask) {
+        if (causal) dqs(bwd_dq_split_kernel<D, true, true, 0>);
+        else dqs(bwd_dq_split_kernel<D, false, true, 0>);
+      } else {
+        if (causal) dqs(bwd_dq_split_kernel<D, true, false, 0>);
+        else dqs(bwd_dq_split_kernel<D, false, false, 0>);
+      }
     } else {
-      if (causal) dqk(bwd_dq_kernel<D, true, false, 0>);
-      else dqk(bwd_dq_kernel<D, false, false, 0>);
+      if (band == 1) dqk(bwd_dq_kernel<D, false, false, 1>);
+      else if (band == 2) dqk(bwd_dq_kernel<D, false, false, 2>);
+      else if (bmask) {
+        if (causal) dqk(bwd_dq_kernel<D, true, true, 0>);
+        else dqk(bwd_dq_kernel<D, false, true, 0>);
+      } else {
+        if (causal) dqk(bwd_dq_kernel<D, true, false, 0>);
+        else dqk(bwd_dq_kernel<D, false, false, 0>);
+      }
     }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
