@@ -477,6 +477,277 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward for d = 256 in two roles (fwd_split_kernel), plain masks only (full
+// attention or causal).
+//
+// With one wave per 32-row slice, the Q fragments (64 registers per lane), the
+// O~ accumulator (128) and the V^T operands (64) oversubscribe a wave's
+// registers; and since the lazy rescale multiplies O~ with vector
+// instructions, the compiler keeps O~ in VGPRs and copies it into AGPRs and
+// back around every PV product (some 300 moves per 32 MFMAs).  Here a
+// workgroup of eight waves covers 128 rows, two waves per slice and per SIMD:
+//   * score wave w (0-3) keeps slice w's Q fragments and the softmax state,
+//     forms S^T = K_j Q^T, masks, forms P~ (the same fast and slow paths as
+//     fwd_bf16_kernel) and hands P~ on through LDS as two MFMA fragments, with
+//     the rescale factor of any row whose reference maximum moved;
+//   * PV wave 4+w keeps slice w's O~^T and trails its score wave by one key
+//     block: it applies a rescale when one was handed on, then O~^T +=
+//     V_j^T P~_j^T with V_j^T by transposing reads.  The PV waves also issue the
+//     copies of K and V (inline assembly, two blocks ahead, ring of four stages).
+// At the end the score wave writes lse and hands 1/l~ to the PV wave, which
+// writes O.  Each slice's arithmetic and the order of its sums are those of
+// fwd_bf16_kernel, so the results are the same bits.
+// ---------------------------------------------------------------------------
+template <int D>
+struct FwdSplitLayout {
+  static constexpr int BC = 32;
+  static constexpr int NC = D / 8;
+  static constexpr int RB = D * 2;
+  static constexpr int KST = BC * RB;                  // K (or V) tile, swizzled rows
+  static constexpr int STAGE = 2 * KST;
+  static constexpr int NSTAGE = 4;
+  static constexpr int F_OFF = NSTAGE * STAGE;         // per slot and score wave: P~ (2 KiB), alpha (256 B), flag
+  static constexpr int F_WAVE = 2048 + 256 + 256;
+  static constexpr int F_SLOT = 4 * F_WAVE;
+  static constexpr int E_OFF = F_OFF + 2 * F_SLOT;     // 1/l~ per lane of each score wave, at the end
+  static constexpr int BYTES = E_OFF + 4 * 256;
+  static constexpr int NDS = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int COPIES = STAGE / 1024 / 4;      // 1 KiB copies per PV wave and block
+  static constexpr int K_OFF = 0, V_OFF = KST;
+  static_assert(NC >= 16 && STAGE % 1024 == 0 && COPIES <= 15, "layout");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                      const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ lse, int Tq, int Tk,
+                      float cl2e, int nqb) {
+  using L = FwdSplitLayout<D>;
+  constexpr int BC = L::BC;
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+  auto stage_ptr = [&](int st) { return smem + st * L::STAGE; };
+
+  constexpr bool PAIRED = CAUSAL;
+  const int nblk = gridDim.x;
+  const int wid = blockIdx.x;
+  const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
+  const int npb = PAIRED ? (nqb + 1) / 2 : nqb;     // workgroups per head
+  const int bh = lin / npb;
+  const int pidx = lin % npb;
+  const int npass = (PAIRED && 2 * pidx + 1 < nqb) ? 2 : 1;
+
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int ws = wave & 3;                          // row slice (score wave ws, PV wave 4+ws)
+  const size_t qbase = (size_t)bh * Tq * D;
+  const size_t kbase = (size_t)bh * Tk * D;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass > 0) {
+      wait_lds_all();
+      barrier_keep_vmem();
+    }
+    const int qb = (npass == 2 && pass == 1) ? pidx : nqb - 1 - pidx;
+    const int q0 = qb * kBR;
+    const int qw = q0 + ws * 32;
+    const int myq = qw + lq;
+    int ntile = (Tk + BC - 1) / BC;
+    if (CAUSAL) ntile = min(ntile, (min(q0 + kBR, Tq) - 1) / BC + 1);
+    char* const fslot0 = smem + L::F_OFF + ws * L::F_WAVE;   // slot s: + s * F_SLOT
+
+    if (wave < 4) {
+      // ============================ score waves ============================
+      const rsrc_t rq = make_rsrc(Q + qbase, (unsigned)Tq * D * 2u);
+      bf16x8 qf[L::NDS];
+#pragma unroll
+      for (int ds = 0; ds < L::NDS; ++ds)
+        qf[ds] = as_bf16x8(bload16(rq, ((unsigned)myq * D + ds * 16 + 8 * hf) * 2u));
+      const int kswz_l = kswz<L::NC>(lq);
+      const int kbase_lane = lq * D * 2 + (((kswz_l >> 1) << 5) | ((hf ^ (kswz_l & 1)) << 4));
+      float m_ref = -INFINITY, l_part = 0.f, lr_part = 0.f;
+      barrier_keep_vmem();
+      for (int j = 0; j < ntile; ++j) {
+        if (!CAUSAL || j * BC <= qw + 31) {
+          const char* kst = stage_ptr(j & (L::NSTAGE - 1)) + L::K_OFF;
+          f32x16 s;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+          for (int ds = 0; ds < L::NDS; ++ds) s = mfma32(as_bf16x8(ld16(kst + (kbase_lane ^ (ds << 5)))), qf[ds], s);
+          sched_reads_ahead<L::NDS>();
+          const int k0 = j * BC;
+          if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk)) {
+            int lim = Tk - 1 - k0;
+            if (CAUSAL) lim = min(lim, myq - k0);
+            lim -= 4 * hf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const unsigned m = (unsigned)((lim - (8 * (r >> 2) + (r & 3))) >> 31);
+              const float x = s[r];
+              s[r] = __builtin_bit_cast(float, (m & 0xff800000u) | (~m & __builtin_bit_cast(unsigned, x)));
+            }
+          }
+          bf16x8 pf[2];
+          float ps[4], prs[4];
+          auto weights = [&](float mneg) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ps[e] = -0.f;
+              prs[e] = 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              u32x4 w;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 8 * t + 2 * e;
+                const float p0 = fast_exp2(__builtin_fmaf(s[r], cl2e, mneg));
+                const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], cl2e, mneg));
+                ps[e] += p0 + p1;
+                w[e] = pack_bf16(p0, p1);
+                prs[e] = add_bf16_pair(w[e], prs[e]);
+              }
+              pf[t] = as_bf16x8(w);
+            }
+          };
+          char* fb = fslot0 + (j & 1) * L::F_SLOT;
+          bool rescale = false;
+          float alpha = 1.f;
+          bool need_max = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0ull;
+          if (!need_max) {
+            weights(-m_ref);
+            const float share = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            need_max = __builtin_amdgcn_ballot_w64(!(share <= kMaxWeight)) != 0ull;
+          }
+          if (need_max) {
+            float mq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mq[q] = max2f(max3f(s[4 * q], s[4 * q + 1], s[4 * q + 2]), s[4 * q + 3]);
+            float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
+            mx = half_swap_max(mx) * cl2e;
+            const bool grow = mx > m_ref + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+              alpha = grow ? fast_exp2(m_ref - mx) : 1.f;
+              if (grow) m_ref = mx;
+              l_part *= alpha;
+              lr_part *= alpha;
+              rescale = true;
+            }
+            weights((m_ref == -INFINITY) ? 0.f : -m_ref);
+          }
+          l_part += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+          lr_part += (prs[0] + prs[1]) + (prs[2] + prs[3]);
+          st16(fb + lane * 16, __builtin_bit_cast(u32x4, pf[0]));
+          st16(fb + 1024 + lane * 16, __builtin_bit_cast(u32x4, pf[1]));
+          reinterpret_cast<float*>(fb + 2048)[lane] = alpha;
+          if (lane == 0) reinterpret_cast<unsigned*>(fb + 2304)[0] = rescale ? 1u : 0u;
+        }
+        wait_lds_all();
+        barrier_keep_vmem();
+      }
+      // lse, and 1/l~ for the PV wave
+      const float l_tot = half_swap_sum(l_part);
+      const float lr_tot = half_swap_sum(lr_part);
+      reinterpret_cast<float*>(smem + L::E_OFF + ws * 256)[lane] = 1.f / lr_tot;
+      if (hf == 0 && myq < Tq) lse[(size_t)bh * Tq + myq] = (m_ref + log2f(l_tot)) * kLn2;
+      wait_lds_all();
+      barrier_keep_vmem();
+    } else {
+      // ============================== PV waves =============================
+      // Copies: waves 4-5 move K_j, waves 6-7 V_j (lane l of copy g moves chunk
+      // 64 g + l: row s / NC, stored chunk s % NC, which holds source chunk
+      // (s % NC) ^ swizzle(row), the K and V swizzles of fwd_bf16_kernel).
+      const int gw = wave - 4;
+      const bool is_v = gw >= 2;
+      const uint16_t* const src = is_v ? V : K;
+      unsigned coff[L::COPIES];
+#pragma unroll
+      for (int i = 0; i < L::COPIES; ++i) {
+        const int sidx = ((gw & 1) * L::COPIES + i) * 64 + lane;
+        const int row = sidx / L::NC, cp = sidx % L::NC;
+        coff[i] = (unsigned)(row * D + (cp ^ (is_v ? vswz<L::NC>(row) : kswz<L::NC>(row))) * 8) * 2u;
+      }
+      const unsigned* const co = coff;   // (the host compiler drops a kernel whose lambdas index a captured array)
+      const unsigned lds0 = (unsigned)(size_t)smem;
+      const unsigned c_dst = (is_v ? L::V_OFF : L::K_OFF) + (gw & 1) * L::COPIES * 1024;
+      auto copy_tile = [&](int j, int st) {
+        const int k0 = j < ntile ? j * BC : Tk;
+        const int rows = Tk - k0;
+        const u32x4 r = raw_rsrc(src + kbase + (size_t)(k0 < Tk ? k0 : 0) * D, rows > 0 ? (unsigned)rows * D * 2u : 0u);
+        const unsigned base = lds0 + (unsigned)st * L::STAGE + c_dst;
+#pragma unroll
+        for (int i = 0; i < L::COPIES; ++i) dma16_unseen(r, co[i], base + i * 1024);
+      };
+      const int vg = lane >> 4, vi = lane & 15;
+      const int vrow = 4 * (vg >> 1) + (vi >> 2);
+      const int vc0 = 2 * (vg & 1) + ((vi & 3) >> 1);
+      const int vlane = vrow * L::RB + ((vc0 ^ vswz<L::NC>(vrow)) << 4) + 8 * (vi & 1);
+      f32x16 o[L::NDB];
+#pragma unroll
+      for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+      // O~^T += V_j^T P~_j^T for the block in stage st with its fragments in slot fs
+      auto pv_step = [&](int st, int fs) {
+        const char* fb = fslot0 + fs * L::F_SLOT;
+        if (reinterpret_cast<const unsigned*>(fb + 2304)[0] != 0u) {
+          const float alpha = reinterpret_cast<const float*>(fb + 2048)[lane];
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        const bf16x8 p0 = as_bf16x8(ld16(fb + lane * 16)), p1 = as_bf16x8(ld16(fb + 1024 + lane * 16));
+        const char* vs = stage_ptr(st) + L::V_OFF;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < L::NDB; ++db) {
+            const char* p = vs + (16 * t) * L::RB + (vlane ^ (db << 6));
+            const u32x2 lo = ld8_tr(p), hi = ld8_tr(p + 8 * L::RB);
+            o[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), t ? p1 : p0, o[db]);
+          }
+        sched_read_pairs_ahead<2 * L::NDB, 4, 2>();
+      };
+      copy_tile(0, 0);
+      copy_tile(1, 1);
+      wait_vmem_le<L::COPIES>();
+      barrier_keep_vmem();
+      for (int j = 0; j < ntile; ++j) {
+        copy_tile(j + 2, (j + 2) & (L::NSTAGE - 1));
+        if (j >= 1 && (!CAUSAL || (j - 1) * BC <= qw + 31)) pv_step((j - 1) & (L::NSTAGE - 1), (j - 1) & 1);
+        wait_vmem_le<L::COPIES>();
+        wait_lds_all();
+        barrier_keep_vmem();
+      }
+      if (ntile > 0 && (!CAUSAL || (ntile - 1) * BC <= qw + 31)) pv_step((ntile - 1) & (L::NSTAGE - 1), (ntile - 1) & 1);
+      wait_vmem_all();                                 // no copy may land after the block is done
+      wait_lds_all();
+      barrier_keep_vmem();                             // the score wave's 1/l~ is in LDS
+      if (qw >= Tq || myq >= Tq) continue;
+      const float inv = reinterpret_cast<const float*>(smem + L::E_OFF + ws * 256)[lane];
+#pragma unroll
+      for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * hf;
+          const size_t off = qbase + (size_t)myq * D + d0;
+          if (OUT_F32) {
+            const f32x4 w = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(O) + off) = w;
+          } else {
+            u32x2 w;
+            w[0] = pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+            w[1] = pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+            st8(static_cast<uint16_t*>(O) + off, w);
+          }
+        }
+    }
+  }
+}
+
 template <int D, bool CAUSAL, bool OUT_F32, bool MASKED, int BAND>
 void launch_one(dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* k, const uint16_t* v, void* o,
                 float* lse, int Tq, int Tk, float cl2e, int nqb, const uint8_t* bmask, int H, long long hstride,
@@ -527,6 +798,20 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int
                                             nd, causal);
   } else if (bmask) {
     launch_dtype<D, true>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+  } else if constexpr (D == 256) {
+    // two roles, eight waves per 128-row block; plain causal: query blocks
+    // nqb-1-p and p share a workgroup
+    const dim3 pgrid((unsigned)((long long)((nqb + 1) / 2) * B * H));
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, causal ? pgrid : grid, dim3(512), 0, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
+    };
+    if (causal) {
+      if (out_f32) go(fwd_split_kernel<D, true, true>);
+      else go(fwd_split_kernel<D, true, false>);
+    } else {
+      if (out_f32) go(fwd_split_kernel<D, false, true>);
+      else go(fwd_split_kernel<D, false, false>);
+    }
   } else {
     // plain causal: query blocks nqb-1-p and p share a workgroup
     const dim3 pgrid((unsigned)((long long)((nqb + 1) / 2) * B * H));
