@@ -388,16 +388,21 @@ def main(argv=None):
         kernels[n] = entry
     dom = max(kflops, key=lambda n: dur[n])
     ach = kflops[dom] / (dur[dom] * 1e-3) / 1e12
-    kernel_name = {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_kv_w4_kernel" if d == 256 else "bwd_kv_kernel",
-                   "bwd_post": "bwd_dq_kernel"}[dom]
+    # the kernels each phase launches: d = 256 runs the forward (plain masks) and the dQ
+    # sweep in two wave roles, the key-block sweep in its four-wave form
+    plain = bmask_np is None and w.window is None and cu_np is None
+    knames = {"fwd": "fwd_split_kernel" if d == 256 and plain else "fwd_bf16_kernel",
+              "bwd_main": "bwd_kv_w4_kernel" if d == 256 else "bwd_kv_kernel",
+              "bwd_post": "bwd_dq_split_kernel" if d == 256 else "bwd_dq_kernel"}
+    kernel_name = knames[dom]
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": read_traffic(kernel_name, w.name),
                 "kernel": kernel_name}
     # the forward's own roofline (the kernel the 60%-of-peak target is set on)
     ach_f = kflops["fwd"] / (dur["fwd"] * 1e-3) / 1e12
     roofline_fwd = {"bound": "mfma", "achieved": round(ach_f, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach_f / peak, 4), "traffic": read_traffic("fwd_bf16_kernel", w.name),
-                    "kernel": "fwd_bf16_kernel"}
+                    "frac": round(ach_f / peak, 4), "traffic": read_traffic(knames["fwd"], w.name),
+                    "kernel": knames["fwd"]}
     cpu = None
     if a.cpu_seconds > 0:
         log("[bench] timing the CPU oracle")

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 NAN_BF16 = np.uint16(0x7FC0)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_nan_in_one_query_row_stays_in_that_row(d):
     B, H, T = 1, 2, 300
     r = 137
@@ -38,7 +38,7 @@ def test_nan_in_one_query_row_stays_in_that_row(d):
     assert maxabs(lse[0, 1, keep], Lr[0, 1, keep]) <= TOL_LSE
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("l", [0, 70, 299])
 def test_nan_in_a_key_reaches_only_the_rows_that_see_it(d, l):
     B, H, T = 1, 1, 300

@@ -114,11 +114,12 @@ def test_constant_v_and_zero_query(d):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("causal", [False, True])
-def test_guard_bands_untouched(dtype, causal):
+def test_guard_bands_untouched(dtype, d, causal):
     """Outputs written into the middle of NaN-filled buffers leave the margins alone."""
     t = torch()
-    B, H, Tq, Tk, d = 2, 2, 77, 130, 128
+    B, H, Tq, Tk = 2, 2, 77, 130
     dev, _ = draw(B, H, Tq, Tk, d, dtype, seed=4000, with_do=True)
     tdt = t.bfloat16 if dtype == "bf16" else t.float32
     M = 64
@@ -143,8 +144,9 @@ def test_guard_bands_untouched(dtype, causal):
         assert t.isfinite(inner).all()
 
 
-def test_forward_bitwise_repeatable():
-    B, H, T, d = 2, 4, 1000, 128
+@pytest.mark.parametrize("d", DIMS)
+def test_forward_bitwise_repeatable(d):
+    B, H, T = 2, 4, 1000
     dev, _ = draw(B, H, T, T, d, "bf16", seed=5000)
     O1, L1 = fa.forward(dev["q"], dev["k"], dev["v"], causal=True)
     O2, L2 = fa.forward(dev["q"], dev["k"], dev["v"], causal=True)
