@@ -813,13 +813,12 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 // outside?"), so that each dQ row is summed in registers by one wave and
 // written once, with no atomics and a fixed summation order.
 //
-// One workgroup per (query block, b, h): eight waves and 256 queries for d = 64
-// and 128, four waves (one per SIMD) and 128 queries for d = 256, where the Q
-// and dO fragments and the dQ^T accumulator alone take 256 registers per lane.
-// Each wave owns 32 query rows and keeps their Q and dO fragments (MFMA B
-// operands), lse, D and the float32 dQ^T accumulator in registers for a sweep
-// over key blocks of 64 keys (32 for d = 256) -- causal: up to the block's
-// last query; tiles a wave cannot see are skipped by that wave.  Per key block j:
+// d = 64 and 128 (d = 256 runs bwd_dq_split_kernel below).  One workgroup of
+// eight waves per (256-query block, b, h).  Each wave owns 32 query rows and
+// keeps their Q and dO fragments (MFMA B operands), lse, D and the float32 dQ^T
+// accumulator in registers for a sweep over key blocks of 64 keys -- causal: up
+// to the block's last query; tiles a wave cannot see are skipped by that wave.
+// Per key block j:
 //   * K_j and V_j go HBM -> LDS by buffer_load ... lds (rows XOR-swizzled by
 //     16-byte chunk).  K_j serves both products: row reads for S^T, and
 //     transposing 8-byte reads (one feature per lane, keys in the k-slot order
@@ -833,20 +832,17 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqLayout {
-  static constexpr int WAVES = D == 256 ? 4 : 8;
+  static_assert(D == 64 || D == 128, "d = 256 runs bwd_dq_split_kernel");
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WAVES_PER_SIMD = WAVES / 4;
   static constexpr int BR = 32 * WAVES;                // query rows per workgroup
-  static constexpr int BC = D == 256 ? 32 : 64;        // keys per block
+  static constexpr int BC = 64;                        // keys per block
   static constexpr int NC = D / 8;                     // 16-byte chunks per K/V row
   static constexpr int RB = D * 2;                     // bytes per K/V row
   static constexpr int KST = BC * RB;                  // K (or V) tile, swizzled rows, unpadded
   static constexpr int STAGE = 2 * KST;
-  // d = 256 runs its sweep with the stage as a run-time index, over three stages
-  // filled two key blocks ahead by copies the compiler does not see (it cannot
-  // tell one array's stages apart and would wait for every copy in flight before
-  // each transposing read); d <= 128 unrolls two steps over two stage arrays.
-  static constexpr int NSTAGE = D == 256 ? 3 : 2;
+  static constexpr int NSTAGE = 2;                     // two steps unrolled over two stage arrays
   static constexpr int BYTES = NSTAGE * STAGE;
   static constexpr int NKB = BC / 32;
   static constexpr int NDB = D / 32;
@@ -879,8 +875,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
   // need not wait for the DMA in flight into the other).
   __shared__ __attribute__((aligned(1024))) char stage0[L::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[L::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage2[L::NSTAGE == 3 ? L::STAGE : 1024];
-  auto stage_ptr = [&](int st) -> char* { return st == 0 ? stage0 : st == 1 ? stage1 : stage2; };
+  auto stage_ptr = [&](int st) -> char* { return st == 0 ? stage0 : stage1; };
 
   // Plain causal: workgroup p of a head runs query block nqb-1-p, then block p
   // (the long block first, as in the forward), so every workgroup sweeps about
@@ -964,19 +959,12 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
       const int rows = Tk - k0;
       const unsigned nbytes = rows > 0 ? (unsigned)rows * D * 2u : 0u;
       const uint16_t* const src = kv_src + kbase + (size_t)(k0 < Tk ? k0 : 0) * D;
-      if constexpr (L::NSTAGE == 3) {
-        const u32x4 r = raw_rsrc(src, nbytes);
-        const unsigned base = (unsigned)(size_t)stage_ptr(st) + wave * L::KDMA_W * 1024;
+      const rsrc_t r = make_rsrc(src, nbytes);
 #pragma unroll
-        for (int i = 0; i < L::KDMA_W; ++i) dma16_unseen(r, kvo[i], base + i * 1024);
-      } else {
-        const rsrc_t r = make_rsrc(src, nbytes);
-#pragma unroll
-        for (int i = 0; i < L::KDMA_W; ++i) {
-          const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              r, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, kvo[i], 0, 0, 0);
-        }
+      for (int i = 0; i < L::KDMA_W; ++i) {
+        const int g = wave * L::KDMA_W + i;            // 0 .. 2 KDMA - 1; V's follow K's in the stage
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(stage_ptr(st) + g * 1024), 16, kvo[i], 0, 0, 0);
       }
     };
     // per-lane K/V read offset for k-step ds: chunk (2 ds + hf) ^ swz of row lq
@@ -1050,19 +1038,10 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
     auto first_row = [&](int j) { return j < ntile ? j * BC : Tk; };
     const int j0 = next_tile(jfirst);
     kv_dma(first_row(j0), 0);
-    int j1 = ntile;                                     // NSTAGE 3: the tile after j0, copied ahead too
-    if constexpr (L::NSTAGE == 3) {
-      j1 = next_tile(j0 + 1);
-      kv_dma(first_row(j1), 1);
-      wait_vmem_le<L::KDMA_W>();
-      barrier_keep_vmem();
-    } else {
-      wait_vmem_all();
-      __syncthreads();
-    }
+    wait_vmem_all();
+    __syncthreads();
 
-    // tile j in stage ST; tile jc is copied into stage SC (the next stage with two
-    // stages, two ahead with three)
+    // tile j in stage ST; tile jc is copied into the other stage SC
     auto step = [&](int j, int ST, int jc, int SC) {
       // the mask test comes before the loads of block jn: a branch between those
       // loads and the reads of stage ST would make the compiler wait for the loads
@@ -1092,11 +1071,11 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
             dp = mfma32(va[ds], gf[ds], dp);
           }
           // ten MFMAs of look-ahead (all eight at d = 64): -1.5% at d = 64, no
-          // loss at 128 and 256
+          // loss at 128
           sched_reads_ahead<2 * L::NDS, 2 * L::NDS, 10>();
           // K^T operands of the dQ product, read now so that their latency hides
           // behind the softmax: both k-steps at d = 64, k-step t = 0 only at d = 128
-          // and 256 (all of them at once would spill there)
+          // (all of them at once would spill there)
           const char* ks = stage_ptr(ST) + L::K_OFF + kb * 32 * L::RB;
           bf16x8 ta[2][L::NDB];
 #pragma unroll
@@ -1135,7 +1114,7 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
             sf[t] = as_bf16x8(w);
           }
           // dQ^T += K_j^T dS^T: lane = query column, register = feature row (at
-          // d = 128 and 256 the operands of k-step t = 1 are read here)
+          // d = 128 the operands of k-step t = 1 are read here)
           if constexpr (D != 64) {
 #pragma unroll
             for (int db = 0; db < L::NDB; ++db) {
@@ -1150,33 +1129,12 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
             for (int db = 0; db < L::NDB; ++db) dq[db] = mfma32(ta[t][db], sf[t], dq[db]);
         }
       }
-      if constexpr (L::NSTAGE == 3) {
-        // this wave's copies of the next tile have landed (they complete in issue
-        // order; the ones just issued may still be in flight), and no wave reads
-        // this stage again before the copy two steps on overwrites it
-        wait_vmem_le<L::KDMA_W>();
-        wait_lds_all();
-        barrier_keep_vmem();
-      } else {
-        wait_vmem_all();
-        __syncthreads();
-      }
+      wait_vmem_all();
+      __syncthreads();
     };
 
-    // The three loop forms compile differently; each is used where it needs no
-    // spills.  d <= 128 unrolls two steps so that every stage offset is a
-    // constant; d = 256 runs one step per iteration with the stage offset
-    // computed at run time.
-    if constexpr (D == 256) {
-      for (int j = j0, st = 0; j < ntile;) {
-        const int j2 = next_tile(j1 + 1);
-        step(j, st, j2, st == 0 ? 2 : st - 1);
-        j = j1;
-        j1 = j2;
-        st = st == 2 ? 0 : st + 1;
-      }
-      wait_vmem_all();   // the copies of tiles past the sweep, before this wave copies into the stages again
-    } else if constexpr (MASKED) {
+    // two steps per iteration, so that every stage offset is a constant
+    if constexpr (MASKED) {
       for (int j = j0; j < ntile;) {
         int jn = next_tile(j + 1);
         step(j, 0, jn, 1);
@@ -1230,7 +1188,8 @@ __attribute__((amdgpu_waves_per_eu(DqLayout<D>::WAVES_PER_SIMD))) void bwd_dq_ke
 // K_j and V_j go HBM -> LDS by buffer_load ... lds (inline assembly, unseen by
 // the compiler) two blocks ahead into a ring of four stages; one bare barrier
 // per phase.  Each slice's arithmetic, and the order of its dQ sums, are those
-// of bwd_dq_kernel, so the results are the same bits.
+// of one wave of bwd_dq_kernel; against the one-role form of this sweep at
+// d = 256 that it replaced, the results were the same bits.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqsLayout {
@@ -1512,11 +1471,15 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
         void* dK, void* dV, int B, int H, int Tq, int Tk, float scale, int causal, int o_f32, int grad_f32,
         void* workspace, int phases, hipStream_t stream, const uint8_t* bmask, int mask_heads, int band, int wl,
         int wr, const int* cu, int nd) {
-  using LQ = DqLayout<D>;
+  // query blocks of the dQ sweep: 256 rows (one role), 128 at d = 256 (two roles)
+  constexpr int DQ_BR = [] {
+    if constexpr (D == 256) return DqsLayout<D>::BR;
+    else return DqLayout<D>::BR;
+  }();
   const long long rows = (long long)B * H * Tq;
   const int nkb = (Tk + kBKC - 1) / kBKC;
   const long long nblk = (long long)nkb * B * H;
-  const int nqb = (Tq + LQ::BR - 1) / LQ::BR;
+  const int nqb = (Tq + DQ_BR - 1) / DQ_BR;
   const long long nqblk = (long long)nqb * B * H;
   constexpr int RPB = 256 / (D / 8);           // rows per row-terms block
   const long long nrb = (rows + RPB - 1) / RPB;
@@ -1576,17 +1539,13 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
     // plain causal: query blocks nqb-1-p and p share a workgroup
     const bool paired = causal && !bmask && band == 0;
     const long long ndq = paired ? (long long)((nqb + 1) / 2) * B * H : nqblk;
+    // both kernels run eight waves per workgroup
     auto dqk = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, dim3((unsigned)ndq), dim3(LQ::THREADS), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq,
-                         Tk, scale, cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
-    };
-    // d = 256: the two-role kernel, eight waves per 128 queries (same grid)
-    auto dqs = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, dim3((unsigned)ndq), dim3(512), 0, stream, q, k, v, g, Ln, Dn, dQ, Tq, Tk, scale,
                          cl2e, nqb, grad_f32, bmask, H, mhs, nmk, wl, wr, cu, nd, causal);
     };
+    auto dqs = dqk;
     if constexpr (D == 256) {
-      static_assert(DqsLayout<D>::BR == LQ::BR, "same query blocks");
       if (band == 1) dqs(bwd_dq_split_kernel<D, false, false, 1>);
       else if (band == 2) dqs(bwd_dq_split_kernel<D, false, false, 2>);
       else if (bmask) {
@@ -1597,6 +1556,7 @@ int bwd(const void* Q, const void* K, const void* V, const void* O, const void* 
         else dqs(bwd_dq_split_kernel<D, false, false, 0>);
       }
     } else {
+      static_assert(DqLayout<D>::THREADS == 512, "eight waves");
       if (band == 1) dqk(bwd_dq_kernel<D, false, false, 1>);
       else if (band == 2) dqk(bwd_dq_kernel<D, false, false, 2>);
       else if (bmask) {
