@@ -2,9 +2,11 @@
 //
 // [ZtF] = "FlashAttention", zerotofrontier.app textbook section 12.3.
 //
-// One workgroup owns a block of 128 query rows of one (batch, head) and makes
-// one sweep over the key/value blocks ([ZtF] "The forward pass"); each of its
-// four waves owns 32 query rows, held as MFMA B operands in registers.  Under a
+// fwd_bf16_kernel (d = 64 and 128): one workgroup owns a block of 128 query
+// rows of one (batch, head) and makes one sweep over the key/value blocks
+// ([ZtF] "The forward pass"); each of its four waves owns 32 query rows, held
+// as MFMA B operands in registers.  d = 256 runs fwd_split_kernel, further
+// down, in two wave roles.  Under a
 // plain causal mask a workgroup runs two blocks in turn, a short and a long one,
 // so that all workgroups sweep about the same number of key blocks.
 //
@@ -52,7 +54,6 @@ namespace {
 template <int D> struct FwdCfg;
 template <> struct FwdCfg<64>  { static constexpr int BC = 64; static constexpr int WAVES_PER_EU = 2; };
 template <> struct FwdCfg<128> { static constexpr int BC = 64; static constexpr int WAVES_PER_EU = 2; };
-template <> struct FwdCfg<256> { static constexpr int BC = 32; static constexpr int WAVES_PER_EU = 1; };
 
 constexpr int kWaves = 4;
 constexpr int kBR = 32 * kWaves;     // query rows per workgroup
@@ -102,6 +103,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      const int* __restrict__ cu, int nd, int bcausal) {
   using L = FwdLayout<D>;
   constexpr int BC = L::BC;
+  static_assert(D == 64 || D == 128, "d = 256 runs fwd_split_kernel");
   // One LDS array per pipeline stage: accesses to distinct arrays carry distinct
   // alias scopes, which lets the compiler see that reads of one stage do not
   // touch the DMA in flight into the other (it would wait for the DMA otherwise).
@@ -325,9 +327,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       s_product(s, cur + L::K_OFF);
       // V^T operands of the PV product.  At d = 128 they are read here, so that
       // their latency hides behind the softmax (with the softmax's fast path below,
-      // 255 registers and no spill).  At d = 64 and 256 they are read after it: at
-      // d = 256, with one wave per SIMD, holding them through the softmax costs
-      // more than it hides.
+      // 255 registers and no spill); at d = 64 after it.
       const char* vs = cur + L::V_OFF;
       bf16x8 va[L::NKB][2][L::NDB];
       auto read_va = [&]() {
@@ -478,8 +478,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Forward for d = 256 in two roles (fwd_split_kernel), plain masks only (full
-// attention or causal).
+// Forward for d = 256 in two roles (fwd_split_kernel), under every mask form:
+// full, causal, block mask, sliding window and packed documents.
 //
 // With one wave per 32-row slice, the Q fragments (64 registers per lane), the
 // O~ accumulator (128) and the V^T operands (64) oversubscribe a wave's
@@ -496,8 +496,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 //     V_j^T P~_j^T with V_j^T by transposing reads.  The PV waves also issue the
 //     copies of K and V (inline assembly, two blocks ahead, ring of four stages).
 // At the end the score wave writes lse and hands 1/l~ to the PV wave, which
-// writes O.  Each slice's arithmetic and the order of its sums are those of
-// fwd_bf16_kernel, so the results are the same bits.
+// writes O.  Each slice's arithmetic, masks and the order of its sums are those
+// of one wave of fwd_bf16_kernel with 32-key blocks; against the one-role form
+// at d = 256 that it replaced, the results were the same bits.
 // ---------------------------------------------------------------------------
 template <int D>
 struct FwdSplitLayout {
@@ -520,17 +521,18 @@ struct FwdSplitLayout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool MASKED, int BAND>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ lse, int Tq, int Tk,
-                      float cl2e, int nqb) {
+                      float cl2e, int nqb, const uint8_t* __restrict__ bmask, int H, long long mask_hstride, int nmk,
+                      int wl, int wr, const int* __restrict__ cu, int nd, int bcausal) {
   using L = FwdSplitLayout<D>;
   constexpr int BC = L::BC;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
   auto stage_ptr = [&](int st) { return smem + st * L::STAGE; };
 
-  constexpr bool PAIRED = CAUSAL;
+  constexpr bool PAIRED = CAUSAL && !MASKED && BAND == 0;
   const int nblk = gridDim.x;
   const int wid = blockIdx.x;
   const int lin = (nblk % 8 == 0) ? (wid % 8) * (nblk / 8) + wid / 8 : wid;
@@ -555,6 +557,54 @@ void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     const int myq = qw + lq;
     int ntile = (Tk + BC - 1) / BC;
     if (CAUSAL) ntile = min(ntile, (min(q0 + kBR, Tq) - 1) / BC + 1);
+    int jfirst = 0;                     // first key block any row of the block can see
+    // BAND: this lane's keys klo .. khi; over the slice's rows the largest lo and
+    // the smallest hi (a tile between them needs no element mask)
+    int klo = 0, khi = 0, w_lo = 0, w_hi = 0;
+    if constexpr (BAND != 0) {
+      const Band<BAND> band{wl, wr, cu, nd, bcausal};
+      band.keys(myq, klo, khi);
+      w_lo = band.lo(qw + 31);
+      w_hi = band.hi(qw);
+      const int b_hi = band.hi(min(q0 + kBR, Tq) - 1);
+      ntile = min(ntile, b_hi < 0 ? 0 : b_hi / BC + 1);
+      jfirst = max(0, band.lo(q0)) / BC;
+    }
+    // visited key blocks, as in fwd_bf16_kernel: all from jfirst on, or (block
+    // mask) those whose 128-key mask block is kept for this 128-row block;
+    // next_tile(j) is the first visited block at or after j (ntile when none is
+    // left, or j itself past the sweep without a mask)
+    const uint8_t* mrow = MASKED ? bmask + (bh % H) * mask_hstride + (long long)qb * nmk : nullptr;
+    const int nvw = (nmk + 63) >> 6;
+    int cw = -1;
+    unsigned long long cbits = 0;
+    auto word = [&](int w) {
+      if (w != cw) {
+        cw = w;
+        cbits = mask_word(mrow, 1, nmk, w, lane);
+      }
+      return cbits;
+    };
+    auto next_tile = [&](int j) {
+      if constexpr (MASKED) {
+        if (j >= ntile) return ntile;
+        const int c = (j * BC) >> 7;
+        int w = c >> 6;
+        unsigned long long bits = word(w) & (~0ull << (c & 63));
+        while (bits == 0) {
+          if (++w >= nvw) return ntile;
+          bits = word(w);
+        }
+        const int c2 = w * 64 + (int)__builtin_ctzll(bits);
+        return c2 == c ? j : min(ntile, (c2 << 7) / BC);
+      } else {
+        return j;
+      }
+    };
+    // causal: key blocks wholly past the slice's rows add exact zeros, and both
+    // waves of the slice skip them
+    auto slice_sees = [&](int j) { return !CAUSAL || j * BC <= qw + 31; };
+    const int j0 = next_tile(jfirst);
     char* const fslot0 = smem + L::F_OFF + ws * L::F_WAVE;   // slot s: + s * F_SLOT
 
     if (wave < 4) {
@@ -568,9 +618,10 @@ void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
       const int kbase_lane = lq * D * 2 + (((kswz_l >> 1) << 5) | ((hf ^ (kswz_l & 1)) << 4));
       float m_ref = -INFINITY, l_part = 0.f, lr_part = 0.f;
       barrier_keep_vmem();
-      for (int j = 0; j < ntile; ++j) {
-        if (!CAUSAL || j * BC <= qw + 31) {
-          const char* kst = stage_ptr(j & (L::NSTAGE - 1)) + L::K_OFF;
+      // step k of the sweep: key block j, in stage k % 4, fragments into slot k % 2
+      for (int j = j0, k = 0; j < ntile; j = next_tile(j + 1), ++k) {
+        if (slice_sees(j)) {
+          const char* kst = stage_ptr(k & (L::NSTAGE - 1)) + L::K_OFF;
           f32x16 s;
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -578,7 +629,16 @@ void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
           for (int ds = 0; ds < L::NDS; ++ds) s = mfma32(as_bf16x8(ld16(kst + (kbase_lane ^ (ds << 5)))), qf[ds], s);
           sched_reads_ahead<L::NDS>();
           const int k0 = j * BC;
-          if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk)) {
+          if constexpr (BAND != 0) {
+            // outside the band of some row of the slice (or the key tail): element mask
+            if (!(k0 >= w_lo && k0 + BC - 1 <= w_hi && k0 + BC <= Tk)) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                if (key >= Tk || key < klo || key > khi) s[r] = -INFINITY;
+              }
+            }
+          } else if ((CAUSAL && k0 + BC - 1 > qw) || (k0 + BC > Tk)) {
             int lim = Tk - 1 - k0;
             if (CAUSAL) lim = min(lim, myq - k0);
             lim -= 4 * hf;
@@ -612,7 +672,7 @@ void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
               pf[t] = as_bf16x8(w);
             }
           };
-          char* fb = fslot0 + (j & 1) * L::F_SLOT;
+          char* fb = fslot0 + (k & 1) * L::F_SLOT;
           bool rescale = false;
           float alpha = 1.f;
           bool need_max = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0ull;
@@ -650,8 +710,11 @@ void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
       // lse, and 1/l~ for the PV wave
       const float l_tot = half_swap_sum(l_part);
       const float lr_tot = half_swap_sum(lr_part);
-      reinterpret_cast<float*>(smem + L::E_OFF + ws * 256)[lane] = 1.f / lr_tot;
-      if (hf == 0 && myq < Tq) lse[(size_t)bh * Tq + myq] = (m_ref + log2f(l_tot)) * kLn2;
+      // a row that sees no key (possible only under a block mask or a band) gets O = 0, lse = -inf
+      constexpr bool EMPTY_ROWS = MASKED || BAND != 0;
+      reinterpret_cast<float*>(smem + L::E_OFF + ws * 256)[lane] = (!EMPTY_ROWS || lr_tot > 0.f) ? 1.f / lr_tot : 0.f;
+      if (hf == 0 && myq < Tq)
+        lse[(size_t)bh * Tq + myq] = (!EMPTY_ROWS || l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       wait_lds_all();
       barrier_keep_vmem();
     } else {
@@ -711,18 +774,25 @@ void fwd_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
           }
         sched_read_pairs_ahead<2 * L::NDB, 4, 2>();
       };
-      copy_tile(0, 0);
-      copy_tile(1, 1);
+      // the blocks of steps 1 and 2 (copied next), and of the previous step
+      int j1 = next_tile(j0 + 1);
+      int j2 = next_tile(j1 + 1);
+      copy_tile(j0, 0);
+      copy_tile(j1, 1);
       wait_vmem_le<L::COPIES>();
       barrier_keep_vmem();
-      for (int j = 0; j < ntile; ++j) {
-        copy_tile(j + 2, (j + 2) & (L::NSTAGE - 1));
-        if (j >= 1 && (!CAUSAL || (j - 1) * BC <= qw + 31)) pv_step((j - 1) & (L::NSTAGE - 1), (j - 1) & 1);
+      int jprev = -1, kprev = -1;
+      for (int j = j0, k = 0; j < ntile; j = next_tile(j + 1), ++k) {
+        copy_tile(j2, (k + 2) & (L::NSTAGE - 1));
+        j2 = next_tile(j2 + 1);
+        if (jprev >= 0 && slice_sees(jprev)) pv_step(kprev & (L::NSTAGE - 1), kprev & 1);
+        jprev = j;
+        kprev = k;
         wait_vmem_le<L::COPIES>();
         wait_lds_all();
         barrier_keep_vmem();
       }
-      if (ntile > 0 && (!CAUSAL || (ntile - 1) * BC <= qw + 31)) pv_step((ntile - 1) & (L::NSTAGE - 1), (ntile - 1) & 1);
+      if (jprev >= 0 && slice_sees(jprev)) pv_step(kprev & (L::NSTAGE - 1), kprev & 1);
       wait_vmem_all();                                 // no copy may land after the block is done
       wait_lds_all();
       barrier_keep_vmem();                             // the score wave's 1/l~ is in LDS
@@ -784,39 +854,54 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* lse, int
   // block mask [mask_heads][ceil(Tq/128)][ceil(Tk/128)]; the 128-row blocks are this kernel's query blocks
   const int nmk = (Tk + 127) / 128;
   const long long hstride = mask_heads == 1 ? 0 : (long long)nqb * nmk;
-  if (band == 1) {
-    if (out_f32)
-      launch_one<D, false, true, false, 1>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
-    else
-      launch_one<D, false, false, false, 1>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
-  } else if (band == 2) {
-    if (out_f32)
-      launch_one<D, false, true, false, 2>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, 0, 0, cu,
-                                           nd, causal);
-    else
-      launch_one<D, false, false, false, 2>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, 0, 0, cu,
-                                            nd, causal);
-  } else if (bmask) {
-    launch_dtype<D, true>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
-  } else if constexpr (D == 256) {
-    // two roles, eight waves per 128-row block; plain causal: query blocks
-    // nqb-1-p and p share a workgroup
-    const dim3 pgrid((unsigned)((long long)((nqb + 1) / 2) * B * H));
-    auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, causal ? pgrid : grid, dim3(512), 0, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb);
+  // plain causal: query blocks nqb-1-p and p share a workgroup
+  const dim3 pgrid((unsigned)((long long)((nqb + 1) / 2) * B * H));
+  if constexpr (D == 256) {
+    // every mask form in two roles, eight waves per 128-row block
+    auto go = [&](auto kernel, dim3 g) {
+      hipLaunchKernelGGL(kernel, g, dim3(512), 0, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk,
+                         wl, wr, cu, nd, causal);
     };
-    if (causal) {
-      if (out_f32) go(fwd_split_kernel<D, true, true>);
-      else go(fwd_split_kernel<D, true, false>);
+    if (band == 1) {
+      if (out_f32) go(fwd_split_kernel<D, false, true, false, 1>, grid);
+      else go(fwd_split_kernel<D, false, false, false, 1>, grid);
+    } else if (band == 2) {
+      if (out_f32) go(fwd_split_kernel<D, false, true, false, 2>, grid);
+      else go(fwd_split_kernel<D, false, false, false, 2>, grid);
+    } else if (bmask) {
+      if (causal) {
+        if (out_f32) go(fwd_split_kernel<D, true, true, true, 0>, grid);
+        else go(fwd_split_kernel<D, true, false, true, 0>, grid);
+      } else {
+        if (out_f32) go(fwd_split_kernel<D, false, true, true, 0>, grid);
+        else go(fwd_split_kernel<D, false, false, true, 0>, grid);
+      }
+    } else if (causal) {
+      if (out_f32) go(fwd_split_kernel<D, true, true, false, 0>, pgrid);
+      else go(fwd_split_kernel<D, true, false, false, 0>, pgrid);
     } else {
-      if (out_f32) go(fwd_split_kernel<D, false, true>);
-      else go(fwd_split_kernel<D, false, false>);
+      if (out_f32) go(fwd_split_kernel<D, false, true, false, 0>, grid);
+      else go(fwd_split_kernel<D, false, false, false, 0>, grid);
     }
   } else {
-    // plain causal: query blocks nqb-1-p and p share a workgroup
-    const dim3 pgrid((unsigned)((long long)((nqb + 1) / 2) * B * H));
-    launch_dtype<D, false>(causal ? pgrid : grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb,
-                           nullptr, H, 0, nmk);
+    if (band == 1) {
+      if (out_f32)
+        launch_one<D, false, true, false, 1>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
+      else
+        launch_one<D, false, false, false, 1>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, wl, wr);
+    } else if (band == 2) {
+      if (out_f32)
+        launch_one<D, false, true, false, 2>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, 0, 0,
+                                             cu, nd, causal);
+      else
+        launch_one<D, false, false, false, 2>(grid, stream, q, k, v, O, lse, Tq, Tk, cl2e, nqb, nullptr, H, 0, nmk, 0, 0,
+                                              cu, nd, causal);
+    } else if (bmask) {
+      launch_dtype<D, true>(grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb, bmask, H, hstride, nmk);
+    } else {
+      launch_dtype<D, false>(causal ? pgrid : grid, stream, causal, out_f32, q, k, v, O, lse, Tq, Tk, cl2e, nqb,
+                             nullptr, H, 0, nmk);
+    }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
