@@ -97,11 +97,12 @@ def test_all_ones_mask_is_the_dense_path_bit_for_bit():
             assert t.equal(a, b), causal
 
 
-def test_rows_and_keys_nobody_sees():
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rows_and_keys_nobody_sees(d):
     """An all-zero mask row: O = 0, lse = -inf, dQ = 0 exactly; a key block no kept row
     sees: dK = dV = 0 exactly; an all-zero mask: everything zero, no NaN."""
     t = torch()
-    B, H, Tq, Tk, d = 1, 2, 400, 520, 64
+    B, H, Tq, Tk = 1, 2, 400, 520
     dev, _ = draw(B, H, Tq, Tk, d, "bf16", seed=4600, with_do=True)
     m = np.ones((1, 4, 5), np.uint8)
     m[0, 2, :] = 0                       # query rows 256..383 see nothing
@@ -125,11 +126,12 @@ def test_rows_and_keys_nobody_sees():
         assert t.all(x == 0)
 
 
-def test_causal_rows_whose_kept_blocks_lie_above_the_diagonal():
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_causal_rows_whose_kept_blocks_lie_above_the_diagonal(d):
     """Causal on top of a mask that keeps only blocks right of the diagonal for some rows:
     those rows see no key (-inf, zeros), the rest match the oracle."""
     t = torch()
-    B, H, T, d = 1, 1, 512, 128
+    B, H, T = 1, 1, 512
     dev, f = draw(B, H, T, T, d, "bf16", seed=4700, with_do=True)
     m = np.zeros((1, 4, 4), np.uint8)
     m[0, 0, 2] = 1                       # row block 0: only a block above the diagonal
